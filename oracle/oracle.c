@@ -1,0 +1,224 @@
+/*
+ * oracle.c -- plain, single-threaded CPU oracle (TEST INFRASTRUCTURE ONLY;
+ * see oracle.h).  Each function follows one step of the method as the
+ * pipelined HCCL AllReduce article (bjdmk.com.cn/news/6235379) states it,
+ * in the article's order, with no blocking, fusion or reordering.
+ *
+ * Readings taken where the article is silent (each is also listed in the
+ * design notes):
+ *   R1  the INT8 AllReduce primitive of §2.2.1 is not defined there; its
+ *       reduction step is read as: dequantize each rank's codes with that
+ *       rank's scale, add the contributions in fp32 in rank order 0..W-1
+ *       (a multiply, then an add, two roundings, no fused multiply-add),
+ *       then quantize the sum again with a fresh absmax scale.
+ *   R2  an all-zero unit makes the article's formula divide 0 by 0; the
+ *       scale is then 0 and every code is 0 (also for a subnormal max whose
+ *       scale rounds to 0).
+ *   R3  a quotient g/s that is NaN (only possible when the unit holds a NaN
+ *       or an infinity) gives code 0; IEEE arithmetic is kept everywhere
+ *       else, so an overflowed sum keeps its inf/NaN.
+ *   R4  the chunk plan is exactly torch.chunk(t, k): pieces of ceil(n/k)
+ *       elements, the last one shorter, ceil(n / ceil(n/k)) pieces.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+
+/* §2.1 dynamic_chunk: the chunk count is the tensor's byte size divided by
+ * the base chunk size rounded down to the alignment, at least 1; the pieces
+ * are those of torch.chunk (R4). */
+int oracle_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
+                       int32_t align_bytes, int64_t *off_out, int64_t cap,
+                       int64_t *count_out)
+{
+    if (numel < 1 || elem_bytes < 1 || chunk_bytes < 1 || align_bytes < 1 ||
+        count_out == NULL)
+        return -1;
+    int64_t denom = chunk_bytes - chunk_bytes % align_bytes;
+    if (denom < 1)
+        return -1;
+    int64_t nbytes = numel * (int64_t)elem_bytes;
+    int64_t k = nbytes / denom;
+    if (k < 1)
+        k = 1;
+    /* torch.chunk: split size ceil(n/k); as many pieces as that size needs */
+    int64_t c = (numel + k - 1) / k;
+    int64_t count = (numel + c - 1) / c;
+    *count_out = count;
+    if (off_out == NULL || cap < count + 1)
+        return 1;
+    for (int64_t j = 0; j < count; ++j)
+        off_out[j] = j * c;
+    off_out[count] = numel;
+    return 0;
+}
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * exponent 0: value = fraction * 2^-24; exponent 31: inf (fraction 0) or
+ * NaN; otherwise (1024 + fraction) * 2^(exponent - 25).  Every binary16
+ * value is exactly representable in binary32, so ldexpf is exact here. */
+float oracle_half_to_float(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexpf((float)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* §6.1: the loss-scaled fp16 gradient is unscaled before quantizing; the
+ * unscale is one binary32 multiply by in_mul (1/S).  fp32 input uses
+ * in_mul = 1. */
+void oracle_load(const void *x, int32_t kind, float in_mul, int64_t n, float *g)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float v;
+        if (kind == ORACLE_F16)
+            v = oracle_half_to_float(((const uint16_t *)x)[i]);
+        else
+            v = ((const float *)x)[i];
+        g[i] = v * in_mul;
+    }
+}
+
+static uint32_t f2u(float f)
+{
+    union { float f; uint32_t u; } c;
+    c.f = f;
+    return c.u;
+}
+
+static float u2f(uint32_t u)
+{
+    union { float f; uint32_t u; } c;
+    c.u = u;
+    return c.f;
+}
+
+/* §2.2.1: torch.max(torch.abs(grad)).  |g| is g with its sign bit cleared;
+ * for non-negative binary32 values the bit patterns order like the values,
+ * and NaN patterns sit above +inf, so a NaN anywhere wins (as torch.max
+ * propagates NaN). */
+uint32_t oracle_absmax_bits(const float *g, int64_t len)
+{
+    uint32_t m = 0;
+    for (int64_t i = 0; i < len; ++i) {
+        uint32_t a = f2u(g[i]) & 0x7fffffffu;
+        if (a > m)
+            m = a;
+    }
+    return m;
+}
+
+/* §2.2.1: scale = max|g| / 127.0, a binary32 division (the tensor is fp32
+ * and 127.0 is a Python scalar, so torch keeps fp32). */
+float oracle_scale(uint32_t amax_bits)
+{
+    return u2f(amax_bits) / 127.0f;
+}
+
+/* §2.2.1: clamp(round(g / scale), -128, 127) cast to int8.  torch.round
+ * rounds halves to even, which is rintf under the default rounding mode.
+ * R2: s == 0 gives 0.  R3: NaN quotient gives 0. */
+int8_t oracle_code(float g, float s)
+{
+    if (s == 0.0f)
+        return 0;
+    float t = g / s;
+    if (isnan(t))
+        return 0;
+    float r = rintf(t);
+    if (r < -128.0f)
+        r = -128.0f;
+    if (r > 127.0f)
+        r = 127.0f;
+    return (int8_t)(int)r;
+}
+
+static void quantize_one_unit(const float *g, int64_t len, float s, int8_t *q)
+{
+    for (int64_t i = 0; i < len; ++i)
+        q[i] = oracle_code(g[i], s);
+}
+
+/* quantize_gradient applied to every unit: load, absmax, scale, codes. */
+void oracle_quantize_units(const void *x, int32_t kind, float in_mul, int64_t n,
+                           const int64_t *off, int64_t n_units,
+                           uint32_t *amax_out, float *scale_out, int8_t *q_out)
+{
+    (void)n;
+    int64_t esz = (kind == ORACLE_F16) ? 2 : 4;
+    for (int64_t u = 0; u < n_units; ++u) {
+        int64_t a = off[u], len = off[u + 1] - off[u];
+        float *g = (float *)malloc((size_t)len * sizeof(float));
+        if (g == NULL)
+            abort();
+        oracle_load((const char *)x + a * esz, kind, in_mul, len, g);
+        uint32_t m = oracle_absmax_bits(g, len);
+        float s = oracle_scale(m);
+        if (amax_out)
+            amax_out[u] = m;
+        scale_out[u] = s;
+        quantize_one_unit(g, len, s, q_out + a);
+        free(g);
+    }
+}
+
+/* Same codes from a max already taken (the absmax and quantize steps run as
+ * two separate calls). */
+void oracle_quantize_with_amax(const void *x, int32_t kind, float in_mul,
+                               int64_t n, const int64_t *off, int64_t n_units,
+                               const uint32_t *amax, float *scale_out,
+                               int8_t *q_out)
+{
+    (void)n;
+    int64_t esz = (kind == ORACLE_F16) ? 2 : 4;
+    for (int64_t u = 0; u < n_units; ++u) {
+        int64_t a = off[u], len = off[u + 1] - off[u];
+        float *g = (float *)malloc((size_t)len * sizeof(float));
+        if (g == NULL)
+            abort();
+        oracle_load((const char *)x + a * esz, kind, in_mul, len, g);
+        float s = oracle_scale(amax[u]);
+        scale_out[u] = s;
+        quantize_one_unit(g, len, s, q_out + a);
+        free(g);
+    }
+}
+
+/* R1: the reduction of the INT8 AllReduce (§2.2.1) on one device.  Each
+ * rank's contribution is its code times its unit's scale (one rounding);
+ * contributions are added to a +0 accumulator in rank order (one rounding
+ * each). */
+void oracle_reduce_dequant(const int8_t *const *q, const float *const *s,
+                           int32_t W, int64_t n, const int64_t *off,
+                           int64_t n_units, float *r_out)
+{
+    (void)n;
+    for (int64_t u = 0; u < n_units; ++u) {
+        for (int64_t i = off[u]; i < off[u + 1]; ++i) {
+            float acc = 0.0f;
+            for (int32_t w = 0; w < W; ++w) {
+                float d = (float)q[w][i] * s[w][u];
+                acc = acc + d;
+            }
+            r_out[i] = acc;
+        }
+    }
+}
+
+/* R1: the summed gradient is quantized again, one fresh scale per unit. */
+void oracle_requantize(const float *r, int64_t n, const int64_t *off,
+                       int64_t n_units, float *scale_out, int8_t *q_out)
+{
+    oracle_quantize_units(r, ORACLE_F32, 1.0f, n, off, n_units, NULL,
+                          scale_out, q_out);
+}

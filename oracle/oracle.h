@@ -1,0 +1,90 @@
+/*
+ * oracle.h -- plain, single-threaded CPU oracle for the INT8-compressed
+ * gradient AllReduce compute.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this code: it exists so that tests, the smoke check and the
+ * benchmark's CPU-baseline leg can compare the HIP library against an
+ * independent, obviously correct implementation.  It shares no source with
+ * the HIP library.
+ *
+ * Source of the method: the pipelined HCCL AllReduce article
+ * (bjdmk.com.cn/news/6235379):
+ *   - §2.1  (three-stage pipeline, data chunking): the dynamic_chunk rule,
+ *   - §2.2.1 (gradient quantization compression): quantize_gradient, the
+ *            int8 codes + fp32 scale pair, and the INT8 AllReduce primitive,
+ *   - §6.1  (mixed-precision pipeline): unscale before quantizing.
+ *
+ * All buffers are host memory owned by the caller.  Every function is pure
+ * (no global state) and single-threaded.  Built with -O2 -ffp-contract=off,
+ * no fast-math and no flush-to-zero, so every float operation below is one
+ * IEEE-754 binary32 operation rounded to nearest-even.
+ */
+#ifndef GQ_ORACLE_H
+#define GQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input element kinds. */
+#define ORACLE_F32 0
+#define ORACLE_F16 1
+
+/* Chunk plan (§2.1, dynamic_chunk): the offsets of torch.chunk(t, k) with
+ * k = max(1, numel*elem_bytes // (chunk_bytes - chunk_bytes % align_bytes)).
+ * Writes count+1 offsets to off_out when cap >= count+1 and sets *count_out.
+ * Returns 0 on success, 1 if cap is too small (count still set), -1 on bad
+ * arguments. */
+int oracle_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
+                       int32_t align_bytes, int64_t *off_out, int64_t cap,
+                       int64_t *count_out);
+
+/* IEEE-754 binary16 bit pattern -> binary32 value (exact). */
+float oracle_half_to_float(uint16_t h);
+
+/* Load + unscale (§6.1): g[i] = float(x[i]) * in_mul, one rounding. */
+void oracle_load(const void *x, int32_t kind, float in_mul, int64_t n, float *g);
+
+/* max |g| over g[0..len) as the bit pattern of |g| (sign bit cleared),
+ * compared as unsigned integers: NaN beats +inf beats every finite value. */
+uint32_t oracle_absmax_bits(const float *g, int64_t len);
+
+/* s = max|g| / 127 in binary32 (§2.2.1). */
+float oracle_scale(uint32_t amax_bits);
+
+/* One int8 code (§2.2.1): round(g/s) half-to-even, clamped to [-128, 127].
+ * s == 0 gives 0; a NaN quotient gives 0. */
+int8_t oracle_code(float g, float s);
+
+/* Quantize one gradient with one scale per unit.  Units are the ranges
+ * [off[u], off[u+1]) of g; off[0] == 0, off[n_units] == n.
+ * scale_out[n_units], q_out[n]; amax_out[n_units] may be NULL. */
+void oracle_quantize_units(const void *x, int32_t kind, float in_mul, int64_t n,
+                           const int64_t *off, int64_t n_units,
+                           uint32_t *amax_out, float *scale_out, int8_t *q_out);
+
+/* Quantize with given per-unit absmax bits (no max pass). */
+void oracle_quantize_with_amax(const void *x, int32_t kind, float in_mul,
+                               int64_t n, const int64_t *off, int64_t n_units,
+                               const uint32_t *amax, float *scale_out,
+                               int8_t *q_out);
+
+/* Reduction step of the INT8 AllReduce on one device: for every element,
+ *   r = (((+0 + q_0*s_0) + q_1*s_1) + ...) + q_{W-1}*s_{W-1}
+ * with each product and each sum rounded to binary32, ranks in order.
+ * q[w] points to rank w's n codes, s[w] to its n_units scales. */
+void oracle_reduce_dequant(const int8_t *const *q, const float *const *s,
+                           int32_t W, int64_t n, const int64_t *off,
+                           int64_t n_units, float *r_out);
+
+/* Requantize the reduced sum with the same units: quantize of fp32 r. */
+void oracle_requantize(const float *r, int64_t n, const int64_t *off,
+                       int64_t n_units, float *scale_out, int8_t *q_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_ORACLE_H */
