@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark: one step of the INT8-compressed gradient AllReduce compute on
+one MI355X, for W simulated data-parallel ranks.
+
+A step is the whole per-device hot path on one batch of gradients already
+resident in HBM:
+  1. quantize every rank's gradient (load + unscale, per-unit absmax, scale,
+     int8 codes): gq_quantize with fused maxima, all W ranks in one call;
+  2. reduce the W ranks' dequantized codes in fp32 in rank order and
+     requantize the sum: gq_reduce_requantize (the sum stays on chip).
+The chunk plans and unit tables are built once at set-up (they depend only
+on the tensor shapes).
+
+Prints one JSON line.  The default workload is the ResNet-152 gradient set
+(W = 8 ranks, 467 fp32 layer tensors, one scale per layer tensor, 25 MiB
+buckets); --workload picks another of the five synthetic workloads.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+METRIC = "GB/s gradient input quantized+reduced on 1 MI355X; % of HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def unit_offsets(w, plan):
+    if w.units == "tensor":
+        return w.toff.copy()
+    parts = [np.zeros(1, dtype=np.int64)]
+    for t, size in enumerate(w.sizes):
+        parts.append(plan(int(size), w.elem_bytes)[1:] + w.toff[t])
+    return np.concatenate(parts)
+
+
+def algorithmic_bytes(W, n, e, U):
+    """Bytes the method must move with one read of every input:
+    quantize: W*n*e in + W*n codes out + W*U scales out;
+    reduce+requantize: W*n codes in + W*U scales in + n codes out + U scales out."""
+    bq = W * n * (e + 1) + 4 * W * U
+    br = n * (W + 1) + 4 * W * U + 4 * U
+    return bq, br
+
+
+def cpu_baseline(w, xs, off, kind):
+    """The oracle as it stands (single-threaded C), on the same host inputs."""
+    from oracle import Oracle
+    o = Oracle()
+    t0 = time.perf_counter()
+    o.allreduce_step(xs, kind, off, w.in_mul)
+    dt = time.perf_counter() - t0
+    nbytes = w.W * w.n * w.elem_bytes
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": dt,
+            "sample": "the whole workload (%d ranks x %d elements): quantize, rank-order "
+                      "reduce and requantize, one host thread" % (w.W, w.n)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the simulated ranks all live in one device's "
+              "memory and this build has no multi-GPU exchange; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(2)
+    from datagen import get_workload
+    from gradient_compression_allreduce_amd import gq
+
+    w = get_workload(args.workload, seed=args.seed)
+    kind = 0 if w.kind == "f32" else 1
+    off = unit_offsets(w, gq.gq_plan_chunks)
+    U = off.size - 1
+    # §2.1 chunk plan of every communication buffer (buckets, else tensors)
+    groups = w.buckets if w.buckets else [(t, t + 1) for t in range(len(w.sizes))]
+    n_chunks = 0
+    for a, b in groups:
+        nb = int(w.toff[b] - w.toff[a])
+        n_chunks += len(gq.gq_plan_chunks(nb, w.elem_bytes)) - 1
+
+    log("workload", w.name, "W", w.W, "n", w.n, "units", U, "chunks", n_chunks)
+    t0 = time.perf_counter()
+    xs = [w.fill(r) for r in range(w.W)]
+    log("generated inputs in %.1f s" % (time.perf_counter() - t0))
+    dev = torch.device("cuda")
+    tdt = torch.float32 if kind == 0 else torch.float16
+    dx = []
+    for x in xs:
+        src = torch.from_numpy(x.view(np.float16) if kind == 1 else x)
+        dx.append(src.to(dev))
+    units = gq.gq_units_create(off)
+    scales = [torch.empty(U, dtype=torch.float32, device=dev) for _ in range(w.W)]
+    codes = [torch.empty(w.n, dtype=torch.int8, device=dev) for _ in range(w.W)]
+    s_out = torch.empty(U, dtype=torch.float32, device=dev)
+    q_out = torch.empty(w.n, dtype=torch.int8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    r_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # practical ceiling: a plain device-to-device copy of the same volume
+    bq, br = algorithmic_bytes(w.W, w.n, w.elem_bytes, U)
+    cp_src = torch.empty(int(bq // 2), dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(2):
+        cp_dst.copy_(cp_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cp_src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
+    input_bytes = w.W * w.n * w.elem_bytes
+    value = input_bytes / (ms * 1e-3) / 1e9
+    b_alg = bq + br
+    q_achieved = bq / (q_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kind,
+        "data": "synthetic",
+        "config": {"workload": w.name, "W": w.W, "elements_per_rank": w.n,
+                   "tensors": int(len(w.sizes)), "scale_units": U,
+                   "scale_unit": w.units, "chunks": n_chunks,
+                   "buckets": len(w.buckets) if w.buckets else None,
+                   "seed": args.seed},
+        "hbm_fraction": round(b_alg / (ms * 1e-3) / HBM_PEAK, 4),
+        "algorithmic_bytes_per_step": b_alg,
+        "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gq_quantize (all ranks)",
+                     "achieved": round(q_achieved, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(q_achieved / (HBM_PEAK / 1e9), 4),
+                     "traffic": None},
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same inputs ...")
+        rec["cpu_baseline"] = cpu_baseline(w, xs, off, kind)
+        rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 4)
+        rec["cpu_baseline"]["seconds"] = round(rec["cpu_baseline"]["seconds"], 2)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,390 @@
+// gq_abi.cpp -- the extern "C" boundary of libgq.so: argument checks, the
+// chunk planner, unit tables, error strings and kernel dispatch.
+// Declarations and the contract of every entry point: include/gq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "gq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gq_status fail(gq_status code, const char *op, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(op) + ": " + buf;
+    return code;
+}
+
+gq_status ok() {
+    g_last_error.clear();
+    return GQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The work tables of one slot geometry (see gq::Tile).
+void build_tiles(const std::vector<int64_t> &off, int V, int64_t cap_slots,
+                 std::vector<gq::Tile> &tiles, std::vector<int32_t> &multi,
+                 std::vector<int32_t> &unit_first, int64_t &n_multi_units, int32_t &max_count) {
+    const int64_t U = static_cast<int64_t>(off.size()) - 1;
+    unit_first.resize(U + 1);
+    n_multi_units = 0;
+    max_count = 1;
+    for (int64_t u = 0; u < U; ++u) {
+        const int64_t a = off[u], b = off[u + 1];
+        const int64_t first_slot = a / V, end_slot = (b + V - 1) / V;
+        const int64_t slots = end_slot - first_slot;
+        const int32_t first = static_cast<int32_t>(tiles.size());
+        unit_first[u] = first;
+        if (slots <= cap_slots) {
+            tiles.push_back({a, b, static_cast<int32_t>(u), first, 1, -1});
+            continue;
+        }
+        const int64_t cnt = (slots + cap_slots - 1) / cap_slots;
+        const int32_t slot = static_cast<int32_t>(n_multi_units++);
+        if (cnt > max_count) max_count = static_cast<int32_t>(cnt);
+        for (int64_t m = 0; m < cnt; ++m) {
+            const int64_t sb = (first_slot + m * cap_slots) * V;
+            const int64_t se = (first_slot + (m + 1) * cap_slots) * V;
+            multi.push_back(static_cast<int32_t>(tiles.size()));
+            tiles.push_back({sb > a ? sb : a, se < b ? se : b, static_cast<int32_t>(u), first,
+                             static_cast<int32_t>(cnt), slot});
+        }
+    }
+    unit_first[U] = static_cast<int32_t>(tiles.size());
+}
+
+template <typename T>
+hipError_t upload(T **dst, const std::vector<T> &src) {
+    *dst = nullptr;
+    if (src.empty()) return hipSuccess;
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(dst), src.size() * sizeof(T));
+    if (e != hipSuccess) return e;
+    return hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+void free_table(gq::Table &t) {
+    if (t.d_tiles) (void)hipFree(t.d_tiles);
+    if (t.d_multi) (void)hipFree(t.d_multi);
+    if (t.d_partial) (void)hipFree(t.d_partial);
+    if (t.d_unit_first) (void)hipFree(t.d_unit_first);
+    if (t.d_pub) (void)hipFree(t.d_pub);
+    if (t.d_ctl) (void)hipFree(t.d_ctl);
+    if (t.d_res) (void)hipFree(t.d_res);
+    if (t.d_cnt) (void)hipFree(t.d_cnt);
+    t = gq::Table{};
+}
+
+gq_status check_units(const char *op, const gq_units *u) {
+    if (!u) return fail(GQ_ERR_INVALID, op, "unit table is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    if (dev != u->device)
+        return fail(GQ_ERR_DEVICE, op, "current device %d, unit table lives on device %d", dev,
+                    u->device);
+    return GQ_OK;
+}
+
+gq_status check_ranks(const char *op, int32_t W) {
+    if (W < 1 || W > GQ_MAX_RANKS)
+        return fail(GQ_ERR_INVALID, op, "W = %d outside [1, %d]", W, GQ_MAX_RANKS);
+    return GQ_OK;
+}
+
+template <typename P>
+gq_status check_ptr_array(const char *op, const char *name, P const *arr, int32_t W,
+                          uintptr_t align) {
+    if (!arr) return fail(GQ_ERR_INVALID, op, "%s is NULL", name);
+    for (int32_t w = 0; w < W; ++w) {
+        if (!arr[w]) return fail(GQ_ERR_INVALID, op, "%s[%d] is NULL", name, w);
+        if (!aligned(arr[w], align))
+            return fail(GQ_ERR_ALIGN, op, "%s[%d] = %p is not %d-byte aligned", name, w,
+                        static_cast<const void *>(arr[w]), static_cast<int>(align));
+    }
+    return GQ_OK;
+}
+
+gq_status check_ptr(const char *op, const char *name, const void *p, uintptr_t align) {
+    if (!p) return fail(GQ_ERR_INVALID, op, "%s is NULL", name);
+    if (!aligned(p, align))
+        return fail(GQ_ERR_ALIGN, op, "%s = %p is not %d-byte aligned", name, p,
+                    static_cast<int>(align));
+    return GQ_OK;
+}
+
+gq_status launch_status(const char *op, hipError_t e) {
+    if (e != hipSuccess) return fail(GQ_ERR_HIP, op, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+gq::TableId q_table(gq_dtype dt) { return dt == GQ_F32 ? gq::TAB_Q32 : gq::TAB_Q16; }
+
+#define GQ_TRY(expr)                      \
+    do {                                  \
+        gq_status st_ = (expr);           \
+        if (st_ != GQ_OK) return st_;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *gq_last_error(void) { return g_last_error.c_str(); }
+
+const char *gq_version(void) { return "gq 0.1 (gfx950)"; }
+
+gq_status gq_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
+                         int32_t align_bytes, int64_t *off_out, int64_t cap,
+                         int64_t *count_out) {
+    const char *op = "gq_plan_chunks";
+    if (!count_out) return fail(GQ_ERR_INVALID, op, "count_out is NULL");
+    if (numel < 1) return fail(GQ_ERR_INVALID, op, "numel = %lld < 1", (long long)numel);
+    if (elem_bytes < 1 || chunk_bytes < 1 || align_bytes < 1)
+        return fail(GQ_ERR_INVALID, op, "elem_bytes, chunk_bytes and align_bytes must be >= 1");
+    const int64_t divisor = chunk_bytes - chunk_bytes % align_bytes;
+    if (divisor < 1)
+        return fail(GQ_ERR_INVALID, op, "chunk_bytes %lld rounds down to 0 at alignment %d",
+                    (long long)chunk_bytes, align_bytes);
+    if (numel > (INT64_MAX / 8) / elem_bytes)
+        return fail(GQ_ERR_INVALID, op, "numel * elem_bytes overflows");
+    int64_t k = numel * elem_bytes / divisor;
+    if (k < 1) k = 1;
+    const int64_t piece = (numel + k - 1) / k;      // torch.chunk split size
+    const int64_t count = (numel + piece - 1) / piece;
+    *count_out = count;
+    if (cap < count + 1 || !off_out)
+        return fail(GQ_ERR_CAPACITY, op, "need %lld offsets, capacity %lld",
+                    (long long)(count + 1), (long long)cap);
+    for (int64_t j = 0; j < count; ++j) off_out[j] = j * piece;
+    off_out[count] = numel;
+    return ok();
+}
+
+gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out) {
+    const char *op = "gq_units_create";
+    if (!out) return fail(GQ_ERR_INVALID, op, "out is NULL");
+    *out = nullptr;
+    if (!h_off) return fail(GQ_ERR_INVALID, op, "h_off is NULL");
+    if (n_units < 1 || n_units > (int64_t(1) << 30))
+        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
+    if (h_off[0] != 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld, must be 0", (long long)h_off[0]);
+    for (int64_t u = 0; u < n_units; ++u)
+        if (h_off[u + 1] <= h_off[u])
+            return fail(GQ_ERR_INVALID, op, "h_off not strictly increasing at unit %lld",
+                        (long long)u);
+    const int64_t n = h_off[n_units];
+    if (n > (int64_t(1) << 40)) return fail(GQ_ERR_INVALID, op, "n = %lld above 2^40", (long long)n);
+
+    gq_units *U = new (std::nothrow) gq_units;
+    if (!U) return fail(GQ_ERR_INVALID, op, "out of host memory");
+    if (hipGetDevice(&U->device) != hipSuccess) {
+        delete U;
+        return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    }
+    U->n = n;
+    U->n_units = n_units;
+    std::vector<int64_t> off(h_off, h_off + n_units + 1);
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&U->d_faults), sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(U->d_faults, 0, sizeof(uint32_t));
+    for (int ti = 0; ti < gq::TAB_COUNT && e == hipSuccess; ++ti) {
+        const gq::TableGeom g = gq::kGeom[ti];
+        std::vector<gq::Tile> tiles;
+        std::vector<int32_t> multi, unit_first;
+        gq::Table &t = U->tab[ti];
+        build_tiles(off, g.V, static_cast<int64_t>(g.block) * g.slots, tiles, multi, unit_first,
+                    t.n_multi_units, t.max_count);
+        t.n_tiles = static_cast<int64_t>(tiles.size());
+        t.n_multi = static_cast<int64_t>(multi.size());
+        e = upload(&t.d_tiles, tiles);
+        if (e == hipSuccess) e = upload(&t.d_multi, multi);
+        if (e == hipSuccess) e = upload(&t.d_unit_first, unit_first);
+        const size_t partial_bytes = sizeof(uint32_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_tiles);
+        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_partial), partial_bytes);
+        if (e == hipSuccess) e = hipMemset(t.d_partial, 0, partial_bytes);
+        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_ctl), 4 * sizeof(uint32_t));
+        if (e == hipSuccess) e = hipMemset(t.d_ctl, 0, 4 * sizeof(uint32_t));
+        if (e == hipSuccess && t.n_multi_units > 0) {
+            const size_t pub_bytes = sizeof(uint64_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_tiles);
+            const size_t unit_bytes =
+                sizeof(uint64_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_multi_units);
+            e = hipMalloc(reinterpret_cast<void **>(&t.d_pub), pub_bytes);
+            if (e == hipSuccess) e = hipMemset(t.d_pub, 0, pub_bytes);
+            if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_res), unit_bytes);
+            if (e == hipSuccess) e = hipMemset(t.d_res, 0, unit_bytes);
+            if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_cnt), unit_bytes);
+            if (e == hipSuccess) e = hipMemset(t.d_cnt, 0, unit_bytes);
+        }
+    }
+    if (e != hipSuccess) {
+        (void)gq_units_destroy(U);
+        return fail(GQ_ERR_HIP, op, "device allocation failed: %s", hipGetErrorString(e));
+    }
+    if (hipDeviceSynchronize() != hipSuccess) {
+        (void)gq_units_destroy(U);
+        return fail(GQ_ERR_HIP, op, "synchronize failed");
+    }
+    *out = U;
+    return ok();
+}
+
+gq_status gq_units_destroy(gq_units *u) {
+    if (!u) return ok();
+    for (int k = 0; k < gq::TAB_COUNT; ++k) free_table(u->tab[k]);
+    if (u->d_faults) (void)hipFree(u->d_faults);
+    delete u;
+    return ok();
+}
+
+gq_status gq_units_faults(const gq_units *u, uint64_t *count) {
+    const char *op = "gq_units_faults";
+    if (!count) return fail(GQ_ERR_INVALID, op, "count is NULL");
+    GQ_TRY(check_units(op, u));
+    uint32_t v = 0;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&v, u->d_faults, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(GQ_ERR_HIP, op, "reading the fault counter failed");
+    *count = v;
+    return ok();
+}
+
+gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units) {
+    if (!u) return fail(GQ_ERR_INVALID, "gq_units_info", "unit table is NULL");
+    if (n) *n = u->n;
+    if (n_units) *n_units = u->n_units;
+    return ok();
+}
+
+static gq_status fill_qargs(const char *op, const void *const *x, int32_t W, gq_dtype dt,
+                            float in_mul, gq::QArgs &a) {
+    GQ_TRY(check_ranks(op, W));
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    if (!std::isfinite(in_mul) || !(in_mul > 0.0f))
+        return fail(GQ_ERR_INVALID, op, "in_mul = %g must be finite and > 0", (double)in_mul);
+    GQ_TRY(check_ptr_array(op, "x", x, W, 16));
+    std::memset(&a, 0, sizeof a);
+    for (int32_t w = 0; w < W; ++w) a.x[w] = x[w];
+    a.W = W;
+    a.in_mul = in_mul;
+    return GQ_OK;
+}
+
+// Unit-table check (last, after every pointer check) and the table fields.
+static gq_status bind_qtable(const char *op, const gq_units *u, gq_dtype dt, gq::QArgs &a) {
+    GQ_TRY(check_units(op, u));
+    a.n_units = u->n_units;
+    a.n = u->n;
+    const gq::Table &t = u->tab[q_table(dt)];
+    a.tiles = t.d_tiles;
+    a.n_tiles = t.n_tiles;
+    a.faults = u->d_faults;
+    return GQ_OK;
+}
+
+gq_status gq_absmax(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                    const gq_units *u, uint32_t *amax_bits, gq_stream stream) {
+    const char *op = "gq_absmax";
+    gq::QArgs a;
+    GQ_TRY(fill_qargs(op, x, W, dt, in_mul, a));
+    GQ_TRY(check_ptr(op, "amax_bits", amax_bits, 4));
+    GQ_TRY(bind_qtable(op, u, dt, a));
+    a.amax_out = amax_bits;
+    const gq::Table &t = u->tab[q_table(dt)];
+    return launch_status(op, gq::launch_absmax(a, dt, t, static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_quantize(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                      const gq_units *u, const uint32_t *amax_bits, float *const *scale_out,
+                      int8_t *const *q_out, gq_stream stream) {
+    const char *op = "gq_quantize";
+    gq::QArgs a;
+    GQ_TRY(fill_qargs(op, x, W, dt, in_mul, a));
+    if (amax_bits) GQ_TRY(check_ptr(op, "amax_bits", amax_bits, 4));
+    GQ_TRY(check_ptr_array(op, "scale_out", scale_out, W, 4));
+    GQ_TRY(check_ptr_array(op, "q_out", q_out, W, 16));
+    GQ_TRY(bind_qtable(op, u, dt, a));
+    for (int32_t w = 0; w < W; ++w) {
+        a.scale[w] = scale_out[w];
+        a.q[w] = q_out[w];
+    }
+    a.amax = amax_bits;
+    const gq::Table &t = u->tab[q_table(dt)];
+    return launch_status(op, gq::launch_quantize(a, dt, t, static_cast<hipStream_t>(stream)));
+}
+
+static gq_status fill_rargs(const char *op, const int8_t *const *q, const float *const *scale,
+                            int32_t W, gq::RArgs &a) {
+    GQ_TRY(check_ranks(op, W));
+    GQ_TRY(check_ptr_array(op, "q", q, W, 16));
+    GQ_TRY(check_ptr_array(op, "scale", scale, W, 4));
+    std::memset(&a, 0, sizeof a);
+    for (int32_t w = 0; w < W; ++w) {
+        a.q[w] = q[w];
+        a.scale[w] = scale[w];
+    }
+    a.W = W;
+    return GQ_OK;
+}
+
+gq_status gq_reduce_dequant(const int8_t *const *q, const float *const *scale, int32_t W,
+                            const gq_units *u, float *r_out, gq_stream stream) {
+    const char *op = "gq_reduce_dequant";
+    gq::RArgs a;
+    GQ_TRY(fill_rargs(op, q, scale, W, a));
+    GQ_TRY(check_ptr(op, "r_out", r_out, 16));
+    GQ_TRY(check_units(op, u));
+    a.r = r_out;
+    a.faults = u->d_faults;
+    a.n = u->n;
+    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], false,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_requantize(const float *r, const gq_units *u, float *scale_out, int8_t *q_out,
+                        gq_stream stream) {
+    const char *op = "gq_requantize";
+    const void *x[1] = {r};
+    gq::QArgs a;
+    GQ_TRY(fill_qargs(op, x, 1, GQ_F32, 1.0f, a));
+    GQ_TRY(check_ptr(op, "scale_out", scale_out, 4));
+    GQ_TRY(check_ptr(op, "q_out", q_out, 16));
+    GQ_TRY(bind_qtable(op, u, GQ_F32, a));
+    a.scale[0] = scale_out;
+    a.q[0] = q_out;
+    a.amax = nullptr;
+    return launch_status(op, gq::launch_quantize(a, GQ_F32, u->tab[gq::TAB_Q32],
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale, int32_t W,
+                               const gq_units *u, float *r_out, float *scale_out, int8_t *q_out,
+                               gq_stream stream) {
+    const char *op = "gq_reduce_requantize";
+    gq::RArgs a;
+    GQ_TRY(fill_rargs(op, q, scale, W, a));
+    if (r_out) GQ_TRY(check_ptr(op, "r_out", r_out, 16));
+    GQ_TRY(check_ptr(op, "scale_out", scale_out, 4));
+    GQ_TRY(check_ptr(op, "q_out", q_out, 16));
+    GQ_TRY(check_units(op, u));
+    a.r = r_out;
+    a.faults = u->d_faults;
+    a.n = u->n;
+    a.scale_out = scale_out;
+    a.q_out = q_out;
+    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], true,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,1028 @@
+// gq_kernels.hip -- gfx950 kernels of the INT8-compressed gradient AllReduce
+// compute (pipelined HCCL AllReduce article, bjdmk.com.cn/news/6235379:
+// §2.2.1 absmax scale, int8 codes and the INT8 AllReduce; §6.1 unscale).
+//
+// The work is bandwidth-bound streaming (no dense contraction, so no MFMA).
+// Kernels walk host-built "tiles" (contiguous element ranges of one unit);
+// one work group owns one tile of one rank at a time.  A tile is read with
+// 16-byte loads, one slot of V elements per lane per step, so a wave touches
+// 1 KiB of contiguous memory per load instruction, and the tile stays in
+// registers between the max and the code pass.
+//
+// The hot path is one persistent, cooperatively launched kernel per stage.
+// Work groups take tiles in order from a ticket counter (tickets run over
+// ranks, then tiles in unit order), so the tiles of one unit start at about
+// the same time.  A unit larger than one tile combines its tiles' maxima in
+// device memory (see "cross-work-group max" below) and each of its tiles
+// waits, bounded, for the others, so every input byte is read from HBM
+// once.  A work group blocks only in that wait, and by then it has
+// published every tile it holds of that unit (it may hold the next tile,
+// loaded or summed ahead to overlap memory latency).  So if all work groups
+// were blocked, the earliest unit any of them waits on would have all of
+// its taken tiles published and at least one tile untaken, which needs
+// every one of the G resident work groups to hold one of its tiles: a unit
+// of more than G tiles.  Resident groups are guaranteed by the cooperative
+// launch, and units of more than G tiles take a two-launch fallback (per-tile
+// maxima, then a re-reading quantize pass).
+//
+// Numerics (must match the CPU oracle bit for bit):
+//   * g = x * in_mul is one rounded binary32 multiply (skipped when
+//     in_mul == 1, which is exact);
+//   * max|g| is an unsigned max over bit patterns with the sign cleared,
+//     taken on the raw inputs and scaled once (rounding is monotonic, so
+//     max_i fl(|x_i| m) = fl(max_i |x_i| m));
+//   * scale = max / 127 is an IEEE division;
+//   * the code is round-half-even of the IEEE quotient g / scale, clamped
+//     to [-128, 127]; NaN quotients give 0 and a zero scale gives 0.  For a
+//     normal scale (2^-126 <= s <= 2^126, so |g/s| <= 128) the quotient is
+//     first estimated as q0 = fl(g * fl(1/s)), within 2^-16 of g/s; when q0
+//     is more than 2^-15 away from every half-integer, fl(g/s) rounds to the
+//     same integer as q0 and the division is skipped, otherwise it is done
+//     exactly;
+//   * the reduction adds fl(q_w * s_w) to a +0 accumulator in rank order
+//     with separate rounded multiplies and adds (never contracted).  The
+//     product is formed as fma(q_w + 128, s_w, -128 s_w), whose single
+//     rounding of the exact value (q_w + 128 - 128) s_w equals fl(q_w s_w)
+//     when 128 s_w does not overflow (|s_w| < 2^121); otherwise it is a
+//     plain multiply.
+#include <hip/hip_fp16.h>
+
+#include "gq_internal.h"
+
+namespace gq {
+namespace {
+
+constexpr uint32_t kAbsMask = 0x7fffffffu;
+constexpr float kNearHalf = 0.5f - 0x1p-15f;   // fast-path guard band
+constexpr uint32_t kSpinLimit = 1u << 20;       // bounded wait (about a second)
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// threadIdx.x as a value the compiler cannot see through, so that per-lane
+// index arithmetic is not hoisted out of the persistent loops (hoisted
+// values stay live across the whole loop and cost registers).
+__device__ __forceinline__ int64_t opaque_tid() {
+    int v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(static_cast<int>(threadIdx.x)));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = umax(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64)));
+    return v;
+}
+
+// Max over the work group; every thread gets it.  `sh` may be reused only
+// after a __syncthreads().
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *sh) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t r = sh[0];
+#pragma unroll
+    for (int i = 1; i < BLOCK / 64; ++i) r = umax(r, sh[i]);
+    return r;
+}
+
+// ---- codes --------------------------------------------------------------------
+
+// Code of g for scale s by the definition (any s != 0, any g).
+__device__ __forceinline__ int code_exact(float g, float s) {
+    const float t = __fdiv_rn(g, s);
+    float r = __builtin_rintf(t);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (t == t) ? static_cast<int>(r) : 0;
+}
+
+// Code of g for a normal scale s with |g| <= max (so |g/s| <= 128) and
+// r = fl(1/s): see the header comment for why this equals code_exact.
+__device__ __forceinline__ int code_fast(float g, float s, float r) {
+    const float q0 = __fmul_rn(g, r);
+    float c = __builtin_rintf(q0);
+    const float d = fabsf(__fsub_rn(q0, c));
+    if (d >= kNearHalf) c = __builtin_rintf(__fdiv_rn(g, s));
+    return static_cast<int>(c);
+}
+
+enum CodeMode { CM_ZERO = 0, CM_FAST = 1, CM_EXACT = 2 };
+
+struct QuantParams {
+    float s, r;
+    int mode;
+};
+
+// `true_max`: the scale comes from the data's own max (fast path allowed).
+__device__ __forceinline__ QuantParams quant_params(float s, bool true_max) {
+    QuantParams p;
+    p.s = s;
+    p.r = 0.0f;
+    if (s == 0.0f) {
+        p.mode = CM_ZERO;
+    } else if (true_max && s >= 0x1p-126f && s <= 0x1p126f) {
+        p.mode = CM_FAST;
+        p.r = __fdiv_rn(1.0f, s);
+    } else {
+        p.mode = CM_EXACT;
+    }
+    return p;
+}
+
+__device__ __forceinline__ uint32_t pack4(int c0, int c1, int c2, int c3) {
+    return (static_cast<uint32_t>(c0) & 0xffu) | ((static_cast<uint32_t>(c1) & 0xffu) << 8) |
+           ((static_cast<uint32_t>(c2) & 0xffu) << 16) | (static_cast<uint32_t>(c3) << 24);
+}
+
+// ---- input slots --------------------------------------------------------------
+// A tile's slots are held raw (as loaded); elements outside the tile read as
+// zero and are never loaded, stored or allowed into a max.
+
+template <typename TIn>
+struct In;
+
+// Rare paths (the last slot of a buffer, slots cut by a unit boundary) are
+// rolled loops, to keep the unrolled hot loops small.
+__device__ __forceinline__ uint4 load_tail16(const void *base, int64_t byte0, int64_t nbytes) {
+    const uint8_t *p = static_cast<const uint8_t *>(base);
+    uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+        if (byte0 + k >= nbytes) break;
+        const uint32_t b = static_cast<uint32_t>(p[byte0 + k]) << (8 * (k & 3));
+        const int wi = k >> 2;
+        w0 |= wi == 0 ? b : 0u;
+        w1 |= wi == 1 ? b : 0u;
+        w2 |= wi == 2 ? b : 0u;
+        w3 |= wi == 3 ? b : 0u;
+    }
+    return make_uint4(w0, w1, w2, w3);
+}
+
+// Keep the bytes [lo, hi) of a 16-byte slot, zero the others.
+__device__ __forceinline__ uint4 keep_bytes(uint4 v, int lo, int hi) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = 4 * k + b;
+            if (i >= lo && i < hi) m |= 0xffu << (8 * b);
+        }
+        w[k] &= m;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 16-byte slot j of an element buffer of n elements of esz bytes, with the
+// elements outside [b, e) zeroed.
+__device__ __forceinline__ uint4 load_slot16(const void *x, int64_t j, int64_t b, int64_t e,
+                                             int64_t n, int esz) {
+    const int per = 16 / esz;
+    const int64_t i0 = j * per;
+    uint4 v;
+    if (i0 + per <= n) v = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + 16 * j);
+    else v = load_tail16(x, 16 * j, n * esz);
+    if (i0 < b || i0 + per > e) {
+        const int lo = static_cast<int>((b > i0 ? b - i0 : 0) * esz);
+        const int hi = static_cast<int>((e < i0 + per ? e - i0 : per) * esz);
+        v = keep_bytes(v, lo, hi);
+    }
+    return v;
+}
+
+template <>
+struct In<float> {
+    static constexpr int V = 4;
+    using Raw = uint4;
+    static __device__ __forceinline__ Raw load(const void *x, int64_t j, int64_t b, int64_t e,
+                                               int64_t n) {
+        return load_slot16(x, j, b, e, n, 4);
+    }
+    static __device__ __forceinline__ uint32_t absmax(const Raw &r, uint32_t m) {
+        m = umax(m, r.x & kAbsMask);
+        m = umax(m, r.y & kAbsMask);
+        m = umax(m, r.z & kAbsMask);
+        return umax(m, r.w & kAbsMask);
+    }
+    // raw max bits -> max |g| (g = x * in_mul)
+    static __device__ __forceinline__ float max_value(uint32_t mbits, float in_mul, bool mul) {
+        const float m = __uint_as_float(mbits);
+        return mul ? __fmul_rn(m, in_mul) : m;
+    }
+    static __device__ __forceinline__ float elem(const Raw &r, int k) {
+        return __uint_as_float(k == 0 ? r.x : k == 1 ? r.y : k == 2 ? r.z : r.w);
+    }
+};
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
+}
+
+template <>
+struct In<__half> {
+    static constexpr int V = 8;
+    using Raw = uint4;
+    static __device__ __forceinline__ Raw load(const void *x, int64_t j, int64_t b, int64_t e,
+                                               int64_t n) {
+        return load_slot16(x, j, b, e, n, 2);
+    }
+    static __device__ __forceinline__ uint32_t absmax(const Raw &r, uint32_t m) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = umax(m, w[k] & 0x7fffu);
+            m = umax(m, (w[k] >> 16) & 0x7fffu);
+        }
+        return m;
+    }
+    static __device__ __forceinline__ float max_value(uint32_t mbits, float in_mul, bool mul) {
+        const float m = h2f(mbits);
+        return mul ? __fmul_rn(m, in_mul) : m;
+    }
+    static __device__ __forceinline__ float elem(const Raw &r, int k) {
+        const uint32_t w = k < 2 ? r.x : k < 4 ? r.y : k < 6 ? r.z : r.w;
+        return h2f((k & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+};
+
+// The slot j of a tile when it is not a whole slot inside the tile: zero
+// past the tile, the buffer's last (short) slot byte by byte, and the
+// elements outside [b, e) cleared.  Rare; kept out of the issue loop.
+template <typename TIn>
+__device__ __forceinline__ uint4 fix_slot(const void *x, int64_t j, int64_t j1, int64_t b,
+                                          int64_t e, int64_t n) {
+    if (j >= j1) return make_uint4(0, 0, 0, 0);
+    return load_slot16(x, j, b, e, n, 16 / In<TIn>::V);
+}
+
+// Issue the loads of the S slots of tile t, at indices clamped into the
+// buffer and without branches, so that all S loads are in flight together.
+template <typename TIn, int S, int BLOCK>
+__device__ __forceinline__ void issue_tile(const void *x, const Tile &t, int64_t n,
+                                           typename In<TIn>::Raw (&raw)[S]) {
+    constexpr int V = In<TIn>::V;
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / V;
+    const int64_t nfull = n / V;
+    const uint4 *xv = static_cast<const uint4 *>(x);
+    if (nfull > 0) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+            raw[s] = xv[j < nfull ? j : nfull - 1];
+        }
+    }
+}
+
+// Redo the few slots that are not whole slots inside the tile, and return
+// the max |x| bits of the tile.
+template <typename TIn, int S, int BLOCK>
+__device__ __forceinline__ uint32_t fix_tile(const void *x, const Tile &t, int64_t n,
+                                             typename In<TIn>::Raw (&raw)[S]) {
+    constexpr int V = In<TIn>::V;
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        const bool inner = j < j1 && j * V >= t.begin && j * V + V <= t.end;
+        if (!inner) raw[s] = fix_slot<TIn>(x, j, j1, t.begin, t.end, n);
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) m = In<TIn>::absmax(raw[s], m);
+    return m;
+}
+
+template <typename TIn, int S, int BLOCK>
+__device__ __forceinline__ uint32_t load_tile(const void *x, const Tile &t, int64_t n,
+                                              typename In<TIn>::Raw (&raw)[S]) {
+    issue_tile<TIn, S, BLOCK>(x, t, n, raw);
+    return fix_tile<TIn, S, BLOCK>(x, t, n, raw);
+}
+
+// Store the packed codes of elements [i0, i0+cnt) that fall inside [b, e).
+__device__ __forceinline__ void store_codes_part(int8_t *q, int64_t i0, int cnt, int64_t b,
+                                                 int64_t e, uint4 packed) {
+#pragma unroll 1
+    for (int k = 0; k < cnt; ++k) {
+        const int64_t i = i0 + k;
+        const uint32_t w = (k >> 2) == 0 ? packed.x : (k >> 2) == 1 ? packed.y
+                         : (k >> 2) == 2 ? packed.z : packed.w;
+        if (i >= b && i < e) q[i] = static_cast<int8_t>((w >> (8 * (k & 3))) & 0xffu);
+    }
+}
+
+// Store the sums of elements [i0, i0+16) that fall inside [b, e).
+__device__ __forceinline__ void store_sum_part(float *r, int64_t i0, int64_t b, int64_t e,
+                                               float4 a0, float4 a1, float4 a2, float4 a3) {
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+        const int64_t i = i0 + k;
+        const float4 v = (k >> 2) == 0 ? a0 : (k >> 2) == 1 ? a1 : (k >> 2) == 2 ? a2 : a3;
+        const float f = (k & 3) == 0 ? v.x : (k & 3) == 1 ? v.y : (k & 3) == 2 ? v.z : v.w;
+        if (i >= b && i < e) r[i] = f;
+    }
+}
+
+// Code of one element for a code mode fixed at compile time.
+template <int MODE>
+__device__ __forceinline__ int code_of(float g, const QuantParams &p) {
+    if constexpr (MODE == CM_FAST) return code_fast(g, p.s, p.r);
+    else if constexpr (MODE == CM_EXACT) return code_exact(g, p.s);
+    else return 0;
+}
+
+// Codes of the S held slots of tile t, for one code mode.
+template <typename TIn, int S, int BLOCK, bool MUL, int MODE>
+__device__ __forceinline__ void quantize_tile_mode(const typename In<TIn>::Raw (&raw)[S],
+                                                   const Tile &t, float in_mul,
+                                                   const QuantParams &p, int8_t *q) {
+    constexpr int V = In<TIn>::V;
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        if (j >= j1) continue;
+        int c[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            float g = In<TIn>::elem(raw[s], k);
+            if (MUL) g = __fmul_rn(g, in_mul);
+            c[k] = code_of<MODE>(g, p);
+        }
+        const int64_t i0 = j * V;
+        if constexpr (V == 4) {
+            const uint32_t p0 = pack4(c[0], c[1], c[2], c[3]);
+            if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint32_t *>(q + i0) = p0;
+            else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, 0, 0, 0));
+        } else {
+            const uint32_t p0 = pack4(c[0], c[1], c[2], c[3]), p1 = pack4(c[4], c[5], c[6], c[7]);
+            if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint2 *>(q + i0) = make_uint2(p0, p1);
+            else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, p1, 0, 0));
+        }
+    }
+}
+
+// The code mode is uniform over the work group: branch once per tile.
+template <typename TIn, int S, int BLOCK, bool MUL>
+__device__ __forceinline__ void quantize_tile(const typename In<TIn>::Raw (&raw)[S], const Tile &t,
+                                              float in_mul, const QuantParams &p, int8_t *q) {
+    const int mode = __builtin_amdgcn_readfirstlane(p.mode);
+    if (mode == CM_FAST) quantize_tile_mode<TIn, S, BLOCK, MUL, CM_FAST>(raw, t, in_mul, p, q);
+    else if (mode == CM_EXACT) quantize_tile_mode<TIn, S, BLOCK, MUL, CM_EXACT>(raw, t, in_mul, p, q);
+    else quantize_tile_mode<TIn, S, BLOCK, MUL, CM_ZERO>(raw, t, in_mul, p, q);
+}
+
+// ---- cross-work-group max of a multi-tile unit ----------------------------------
+// Each tile of a multi-tile unit publishes its max in its own 64-bit word,
+// tagged with the launch's tag in the high half, then counts itself in on
+// the unit's arrival counter.  The tile that completes a multiple of the
+// unit's tile count is the last to arrive: it reads every tile word of the
+// unit (waiting for any not yet visible), and publishes the unit max in the
+// unit's tagged result word, which the other tiles poll.  All accesses are
+// relaxed device-scope atomics on the words that carry the data, so no
+// acquire/release fences (which would write back or invalidate the L2) are
+// needed, and nothing has to be cleared between launches: a word holding an
+// earlier launch's tag reads as "not yet published", and every launch adds
+// exactly the tile count to each unit's counter.
+//
+// The tag is the table's launch epoch with the top bit set (never the
+// initial zero); the last work group to leave a launch advances the epoch.
+// A stale word could only pass for a fresh one after 2^31 launches of the
+// table without that word being rewritten.
+
+__device__ __forceinline__ uint32_t launch_tag(const uint32_t *ctl) {
+    return __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) | 0x80000000u;
+}
+
+// Thread 0: take the next ticket (every work group takes tickets until one
+// is past the end, so a launch advances the counter by total + G; the last
+// work group to leave clears it).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctl) {
+    return __hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the work group, once, at the end of a persistent kernel.
+__device__ __forceinline__ void launch_exit(uint32_t *ctl) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&ctl[1], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&ctl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Poll `word` (by lane 0) until it carries `tag`; returns its low half.
+__device__ __forceinline__ uint32_t wait_tagged(const uint64_t *word, uint32_t tag, bool give_up,
+                                                uint32_t *faults) {
+    uint64_t v = 0;
+    for (uint32_t it = 0;; ++it) {
+        v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (static_cast<uint32_t>(v >> 32) == tag) break;
+        if (give_up || it >= kSpinLimit) {
+            __hip_atomic_fetch_add(faults, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return static_cast<uint32_t>(v);
+}
+
+// Wave 0: publish this tile's max m and count the tile in.  Returns (in
+// lane 0) the unit's arrival count after this tile; a multiple of the tile
+// count means this tile was the unit's last to arrive.
+__device__ __forceinline__ uint64_t unit_publish(uint64_t *pub, uint64_t *cnt, int32_t tix,
+                                                 uint32_t m, uint32_t tag) {
+    uint64_t arrived = 0;
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&pub[tix], (static_cast<uint64_t>(tag) << 32) | m, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    }
+    return arrived;
+}
+
+// Wave 0: the unit max.  The unit's last arrival gathers every tile's max
+// and publishes the unit max in the result word; the others poll that word.
+__device__ __forceinline__ uint32_t unit_max(uint64_t *pub, uint64_t *res, int32_t tix,
+                                             int32_t first, int32_t count, uint32_t m,
+                                             uint64_t arrived_lane0, uint32_t tag,
+                                             uint32_t *faults) {
+    const int lane = threadIdx.x;
+    const uint64_t arrived = __shfl(arrived_lane0, 0, 64);
+    // after a wait has given up once, later waits do not wait again
+    const bool give_up = __hip_atomic_load(faults, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    if (arrived % static_cast<uint64_t>(count) != 0) {
+        uint32_t um = 0;
+        if (lane == 0) um = wait_tagged(res, tag, give_up, faults);
+        return static_cast<uint32_t>(__shfl(static_cast<int>(um), 0, 64));
+    }
+    uint32_t mx = m;
+    for (int i = lane; i < count; i += 64) {
+        if (first + i == tix) continue;
+        mx = umax(mx, wait_tagged(&pub[first + i], tag, give_up, faults));
+    }
+    mx = wave_max(mx);
+    if (lane == 0)
+        __hip_atomic_store(res, (static_cast<uint64_t>(tag) << 32) | mx, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    return mx;
+}
+
+// Tile descriptors are read-only: load them through the scalar cache.
+__device__ __forceinline__ Tile load_desc(const Tile *tiles, int64_t i) {
+    using ConstTile = __attribute__((address_space(4))) const Tile;
+    const ConstTile *p = (const ConstTile *)(tiles + i);
+    Tile t;
+    t.begin = p->begin;
+    t.end = p->end;
+    t.unit = p->unit;
+    t.first = p->first;
+    t.count = p->count;
+    t.slot = p->slot;
+    return t;
+}
+
+// ---- quantize kernels -------------------------------------------------------------
+
+// Hot path: every tile of every rank, one read of the input.  A work group
+// loads its next tile and publishes that tile's max before it waits for the
+// current tile's unit max, so that it never blocks while holding an
+// unpublished tile (see the scheduling note above) and the wait overlaps the
+// next tile's loads.
+template <typename TIn, int S, int BLOCK, bool MUL>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void k_quantize_coop(const QArgs a) {
+    using Raw = typename In<TIn>::Raw;
+    __shared__ uint32_t sh[BLOCK / 64];
+    __shared__ uint32_t s_val[2];  // unit max, next ticket
+    const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
+    const uint32_t tag = launch_tag(a.ctl);
+    if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+    __syncthreads();
+    int64_t tk = s_val[1];
+    Raw cur[S], nxt[S];
+    Tile tc{};
+    int wc = 0;
+    uint32_t mc = 0;          // cur's own max
+    uint64_t arr_c = 0;       // cur's arrival count (lane 0 of wave 0)
+    // load a tile, take its max and publish it (wave 0 gathers at once if it
+    // was the unit's last arrival)
+    auto start_tile = [&](int64_t t_k, Raw (&buf)[S], Tile &t, int &w, uint32_t &m, uint64_t &arr) {
+        w = static_cast<int>(t_k / a.n_tiles);
+        const int32_t tix = static_cast<int32_t>(t_k - static_cast<int64_t>(w) * a.n_tiles);
+        t = load_desc(a.tiles, tix);
+        issue_tile<TIn, S, BLOCK>(a.x[w], t, a.n, buf);
+        m = block_max<BLOCK>(fix_tile<TIn, S, BLOCK>(a.x[w], t, a.n, buf), sh);
+        if (t.count > 1 && threadIdx.x < 64) {
+            uint64_t *pub = a.pub + static_cast<int64_t>(w) * a.n_tiles;
+            const int64_t u = static_cast<int64_t>(w) * a.n_multi_units + t.slot;
+            arr = unit_publish(pub, a.cnt + u, tix, m, tag);
+            if (__shfl(arr, 0, 64) % static_cast<uint64_t>(t.count) == 0)
+                (void)unit_max(pub, a.res + u, tix, t.first, t.count, m, arr, tag, a.faults);
+        }
+    };
+    if (tk < total) start_tile(tk, cur, tc, wc, mc, arr_c);
+    while (tk < total) {
+        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+        __syncthreads();
+        const int64_t tn = s_val[1];
+        const bool more = tn < total;
+        Tile tnx{};
+        int wn = 0;
+        uint32_t mn = 0;
+        uint64_t arr_n = 0;
+        if (more) start_tile(tn, nxt, tnx, wn, mn, arr_n);
+        const int32_t tix = static_cast<int32_t>(tk - static_cast<int64_t>(wc) * a.n_tiles);
+        uint32_t m = mc;
+        if (tc.count > 1) {
+            if (threadIdx.x < 64) {
+                const int64_t u = static_cast<int64_t>(wc) * a.n_multi_units + tc.slot;
+                const uint32_t um = unit_max(a.pub + static_cast<int64_t>(wc) * a.n_tiles, a.res + u,
+                                             tix, tc.first, tc.count, mc, arr_c, tag, a.faults);
+                if (threadIdx.x == 0) s_val[0] = um;
+            }
+            __syncthreads();
+            m = s_val[0];
+        }
+        const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
+        if (threadIdx.x == 0 && tix == tc.first) a.scale[wc][tc.unit] = sc;
+        quantize_tile<TIn, S, BLOCK, MUL>(cur, tc, a.in_mul, quant_params(sc, true), a.q[wc]);
+        __syncthreads();
+        if (!more) break;
+#pragma unroll
+        for (int s = 0; s < S; ++s) cur[s] = nxt[s];
+        tc = tnx;
+        wc = wn;
+        tk = tn;
+        mc = mn;
+        arr_c = arr_n;
+    }
+    launch_exit(a.ctl);
+}
+
+// Fallback pass 1 (and gq_absmax): per-tile max of the listed tiles.
+template <typename TIn, int S, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_tile_absmax(const QArgs a) {
+    __shared__ uint32_t sh[BLOCK / 64];
+    const int w = blockIdx.y;
+    const int32_t tix = a.list ? a.list[blockIdx.x] : static_cast<int32_t>(blockIdx.x);
+    const Tile t = load_desc(a.tiles, tix);
+    typename In<TIn>::Raw raw[S];
+    const uint32_t m = block_max<BLOCK>(load_tile<TIn, S, BLOCK>(a.x[w], t, a.n, raw), sh);
+    if (threadIdx.x == 0) a.partial[static_cast<int64_t>(w) * a.n_tiles + tix] = m;
+}
+
+// gq_absmax: one max per (rank, unit) from the per-tile maxima.
+template <typename TIn>
+__global__ void k_absmax_finalize(const QArgs a, bool mul) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<int64_t>(a.W) * a.n_units) return;
+    const int64_t w = idx / a.n_units, u = idx - w * a.n_units;
+    const uint32_t *p = a.partial + w * a.n_tiles;
+    uint32_t m = 0;
+    for (int32_t i = a.unit_first[u]; i < a.unit_first[u + 1]; ++i) m = umax(m, p[i]);
+    a.amax_out[idx] = __float_as_uint(In<TIn>::max_value(m, a.in_mul, mul)) & kAbsMask;
+}
+
+enum QMode { Q_FUSED = 0, Q_GIVEN = 1 };
+
+// Fallback pass 2 (Q_FUSED: maxima from pass 1 for multi-tile units) and
+// the quantize-with-given-maxima entry (Q_GIVEN).  One tile per work group.
+template <typename TIn, int S, int BLOCK, bool MUL, int MODE>
+__global__ __launch_bounds__(BLOCK) void k_quantize(const QArgs a) {
+    __shared__ uint32_t sh[BLOCK / 64];
+    const int w = blockIdx.y;
+    const int32_t tix = static_cast<int32_t>(blockIdx.x);
+    const Tile t = load_desc(a.tiles, tix);
+    typename In<TIn>::Raw raw[S];
+    const uint32_t own = load_tile<TIn, S, BLOCK>(a.x[w], t, a.n, raw);
+    float maxv;
+    if (MODE == Q_GIVEN) {
+        maxv = __uint_as_float(a.amax[static_cast<int64_t>(w) * a.n_units + t.unit]);
+    } else {
+        uint32_t m;
+        if (t.count == 1) {
+            m = block_max<BLOCK>(own, sh);
+        } else {
+            const uint32_t *p = a.partial + static_cast<int64_t>(w) * a.n_tiles + t.first;
+            uint32_t pm = 0;
+            for (int i = threadIdx.x; i < t.count; i += BLOCK) pm = umax(pm, p[i]);
+            m = block_max<BLOCK>(pm, sh);
+        }
+        maxv = In<TIn>::max_value(m, a.in_mul, MUL);
+    }
+    const float sc = __fdiv_rn(maxv, 127.0f);
+    if (threadIdx.x == 0 && tix == t.first) a.scale[w][t.unit] = sc;
+    quantize_tile<TIn, S, BLOCK, MUL>(raw, t, a.in_mul, quant_params(sc, MODE == Q_FUSED), a.q[w]);
+}
+
+// ---- reduce kernels ----------------------------------------------------------------
+
+constexpr int RV = 16;  // codes per reduce slot
+
+// acc += fl(q * sw) for the 16 codes of each held slot.  u = q + 128 is
+// taken from the byte with its top bit flipped (exact as a float).
+template <int S, bool VIA_FMA>
+__device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float neg128,
+                                           float (&acc)[S][RV]) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t wd[4] = {v[s].x ^ 0x80808080u, v[s].y ^ 0x80808080u,
+                                v[s].z ^ 0x80808080u, v[s].w ^ 0x80808080u};
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+            const float u = static_cast<float>((wd[k >> 2] >> (8 * (k & 3))) & 0xffu);
+            const float d = VIA_FMA ? __builtin_fmaf(u, sw, neg128)
+                                    : __fmul_rn(__fsub_rn(u, 128.0f), sw);
+            acc[s][k] = __fadd_rn(acc[s][k], d);
+        }
+    }
+}
+
+// Rank-order dequant-accumulate of the S slots of tile t into acc.
+template <int S, int BLOCK>
+__device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float (&acc)[S][RV]) {
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < RV; ++k) acc[s][k] = 0.0f;
+
+    // Codes are loaded RG ranks at a time, the next group while the current
+    // one is accumulated.  Loads are issued at indices clamped into the
+    // buffer, without branches; slots past the tile or at the buffer's short
+    // end are redone afterwards.  Whole 16-byte slots are read even where a
+    // unit boundary cuts them (the bytes belong to the rank's buffer); sums
+    // of elements outside the tile are cleared below.
+    constexpr int RG = 4;
+    const int64_t nfull = a.n / RV;
+    uint4 cur[RG][S], nxt[RG][S];
+    auto issue = [&](int w0, uint4 (&v)[RG][S]) {
+        if (nfull <= 0) return;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            if (w0 + r >= a.W) break;
+            const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+                v[r][s] = qv[j < nfull ? j : nfull - 1];
+            }
+        }
+    };
+    issue(0, cur);
+    for (int w0 = 0; w0 < a.W; w0 += RG) {
+        if (w0 + RG < a.W) issue(w0 + RG, nxt);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int w = w0 + r;
+            if (w >= a.W) break;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+                if (!(j < j1 && j < nfull))
+                    cur[r][s] = (j < j1) ? load_tail16(a.q[w], j * RV, a.n) : make_uint4(0, 0, 0, 0);
+            }
+            const float sw = a.scale[w][t.unit];
+            const float neg128 = -128.0f * sw;
+            const bool via_fma = fabsf(sw) < 0x1p121f;  // false for inf and NaN too (uniform)
+            if (via_fma) accumulate<S, true>(cur[r], sw, neg128, acc);
+            else accumulate<S, false>(cur[r], sw, neg128, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int s = 0; s < S; ++s) cur[r][s] = nxt[r][s];
+    }
+    // elements outside the tile never reach a max or a store (0 * inf = NaN)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        const int64_t i0 = j * RV;
+        if (!(j < j1 && i0 >= t.begin && i0 + RV <= t.end)) {
+#pragma unroll
+            for (int k = 0; k < RV; ++k) {
+                const int64_t i = i0 + k;
+                if (!(j < j1 && i >= t.begin && i < t.end)) acc[s][k] = 0.0f;
+            }
+        }
+    }
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t acc_absmax(const float (&acc)[S][RV]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < RV; ++k) m = umax(m, __float_as_uint(acc[s][k]) & kAbsMask);
+    return m;
+}
+
+template <int S, int BLOCK>
+__device__ __forceinline__ void store_sum(const Tile &t, const float (&acc)[S][RV], float *r) {
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        if (j >= j1) continue;
+        const int64_t i0 = j * RV;
+        float4 f[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            f[k] = make_float4(acc[s][4 * k], acc[s][4 * k + 1], acc[s][4 * k + 2], acc[s][4 * k + 3]);
+        if (i0 >= t.begin && i0 + RV <= t.end) {
+            float4 *rp = reinterpret_cast<float4 *>(r + i0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rp[k] = f[k];
+        } else {
+            store_sum_part(r, i0, t.begin, t.end, f[0], f[1], f[2], f[3]);
+        }
+    }
+}
+
+template <int S, int BLOCK, int MODE>
+__device__ __forceinline__ void requantize_tile_mode(const Tile &t, const float (&acc)[S][RV],
+                                                     const QuantParams &p, int8_t *q) {
+    const int64_t tid = opaque_tid();
+    const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        if (j >= j1) continue;
+        int c[RV];
+#pragma unroll
+        for (int k = 0; k < RV; ++k) c[k] = code_of<MODE>(acc[s][k], p);
+        const int64_t i0 = j * RV;
+        const uint4 pk = make_uint4(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
+                                    pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15]));
+        if (i0 >= t.begin && i0 + RV <= t.end) *reinterpret_cast<uint4 *>(q + i0) = pk;
+        else store_codes_part(q, i0, RV, t.begin, t.end, pk);
+    }
+}
+
+template <int S, int BLOCK>
+__device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc)[S][RV],
+                                                const QuantParams &p, int8_t *q) {
+    const int mode = __builtin_amdgcn_readfirstlane(p.mode);
+    if (mode == CM_FAST) requantize_tile_mode<S, BLOCK, CM_FAST>(t, acc, p, q);
+    else if (mode == CM_EXACT) requantize_tile_mode<S, BLOCK, CM_EXACT>(t, acc, p, q);
+    else requantize_tile_mode<S, BLOCK, CM_ZERO>(t, acc, p, q);
+}
+
+// Hot path: reduce + requantize of every tile, one read of the codes.  A
+// work group sums its next tile (and publishes that tile's max) before it
+// waits for the current tile's unit max, so the wait overlaps a whole tile
+// of memory traffic.
+template <int S, int BLOCK>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void k_reduce_coop(const RArgs a) {
+    __shared__ uint32_t sh[BLOCK / 64];
+    __shared__ uint32_t s_val[2];  // unit max, next ticket
+    const int64_t total = a.n_tiles;
+    const uint32_t tag = launch_tag(a.ctl);
+    if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+    __syncthreads();
+    int64_t tk = s_val[1];
+    float acc_c[S][RV], acc_n[S][RV];
+    Tile tc{};
+    uint32_t mc = 0;
+    uint64_t arr_c = 0;
+    if (tk < total) {
+        tc = load_desc(a.tiles, tk);
+        reduce_tile<S, BLOCK>(a, tc, acc_c);
+        if (a.r) store_sum<S, BLOCK>(tc, acc_c, a.r);
+        mc = block_max<BLOCK>(acc_absmax<S>(acc_c), sh);
+        if (tc.count > 1 && threadIdx.x < 64)
+            arr_c = unit_publish(a.pub, a.cnt + tc.slot, static_cast<int32_t>(tk), mc, tag);
+    }
+    while (tk < total) {
+        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+        __syncthreads();
+        const int64_t tn = s_val[1];
+        const bool more = tn < total;
+        Tile tnx{};
+        uint32_t mn = 0;
+        uint64_t arr_n = 0;
+        if (more) {
+            tnx = load_desc(a.tiles, tn);
+            reduce_tile<S, BLOCK>(a, tnx, acc_n);
+            if (a.r) store_sum<S, BLOCK>(tnx, acc_n, a.r);
+            mn = block_max<BLOCK>(acc_absmax<S>(acc_n), sh);
+            if (tnx.count > 1 && threadIdx.x < 64) {
+                arr_n = unit_publish(a.pub, a.cnt + tnx.slot, static_cast<int32_t>(tn), mn, tag);
+                if (__shfl(arr_n, 0, 64) % static_cast<uint64_t>(tnx.count) == 0)  // last: gather now
+                    (void)unit_max(a.pub, a.res + tnx.slot, static_cast<int32_t>(tn), tnx.first,
+                                   tnx.count, mn, arr_n, tag, a.faults);
+            }
+        }
+        uint32_t m = mc;
+        if (tc.count > 1) {
+            if (threadIdx.x < 64) {
+                const uint32_t um = unit_max(a.pub, a.res + tc.slot, static_cast<int32_t>(tk),
+                                             tc.first, tc.count, mc, arr_c, tag, a.faults);
+                if (threadIdx.x == 0) s_val[0] = um;
+            }
+            __syncthreads();
+            m = s_val[0];
+        }
+        const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+        if (threadIdx.x == 0 && tk == tc.first) a.scale_out[tc.unit] = sc;
+        requantize_tile<S, BLOCK>(tc, acc_c, quant_params(sc, true), a.q_out);
+        __syncthreads();
+        if (!more) break;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int k = 0; k < RV; ++k) acc_c[s][k] = acc_n[s][k];
+        tc = tnx;
+        mc = mn;
+        arr_c = arr_n;
+        tk = tn;
+    }
+    launch_exit(a.ctl);
+}
+
+enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
+
+// Non-persistent reduce: the plain sum (R_SUM), and the two-launch fallback
+// for units with more tiles than resident work groups (R_PASS1 writes
+// per-tile maxima, R_FUSED recomputes the sum and requantizes).
+template <int S, int BLOCK, int MODE>
+__global__ __launch_bounds__(BLOCK) void k_reduce(const RArgs a) {
+    __shared__ uint32_t sh[BLOCK / 64];
+    const int32_t tix = (MODE == R_PASS1) ? a.list[blockIdx.x] : static_cast<int32_t>(blockIdx.x);
+    const Tile t = load_desc(a.tiles, tix);
+    float acc[S][RV];
+    reduce_tile<S, BLOCK>(a, t, acc);
+    if (a.r != nullptr && (MODE != R_FUSED || t.count == 1)) store_sum<S, BLOCK>(t, acc, a.r);
+    if (MODE == R_SUM) return;
+    uint32_t m;
+    if (MODE == R_PASS1) {
+        m = block_max<BLOCK>(acc_absmax<S>(acc), sh);
+        if (threadIdx.x == 0) a.partial[tix] = m;
+        return;
+    }
+    if (t.count == 1) {
+        m = block_max<BLOCK>(acc_absmax<S>(acc), sh);
+    } else {
+        const uint32_t *p = a.partial + t.first;
+        uint32_t pm = 0;
+        for (int i = threadIdx.x; i < t.count; i += BLOCK) pm = umax(pm, p[i]);
+        m = block_max<BLOCK>(pm, sh);
+    }
+    const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+    if (threadIdx.x == 0 && tix == t.first) a.scale_out[t.unit] = sc;
+    requantize_tile<S, BLOCK>(t, acc, quant_params(sc, true), a.q_out);
+}
+
+// ---- launch helpers -------------------------------------------------------------------
+
+struct DeviceInfo {
+    int cus = 0;
+};
+
+DeviceInfo device_info() {
+    static thread_local int cached_dev = -1;
+    static thread_local DeviceInfo info;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev != cached_dev) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) info.cus = prop.multiProcessorCount;
+        cached_dev = dev;
+    }
+    return info;
+}
+
+// Resident work groups of kernel K on the current device (0 on error),
+// cached per kernel and device.
+template <auto K>
+int64_t resident_groups(int block) {
+    static thread_local int cached_dev = -1;
+    static thread_local int64_t cached = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev == cached_dev) return cached;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, block, 0) != hipSuccess)
+        return 0;
+    cached = static_cast<int64_t>(per_cu) * device_info().cus;
+    cached_dev = dev;
+    return cached;
+}
+
+template <typename K, typename A>
+hipError_t launch_coop(K kernel, int64_t groups, int block, const A &args, hipStream_t s) {
+    A copy = args;
+    void *params[] = {&copy};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
+                                      dim3(static_cast<unsigned>(groups)), dim3(block), params, 0, s);
+}
+
+template <typename TIn, bool MUL>
+hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
+    QArgs a = a0;
+    a.partial = t.d_partial;
+    a.tiles = t.d_tiles;
+    a.pub = t.d_pub;
+    a.res = t.d_res;
+    a.cnt = t.d_cnt;
+    a.ctl = t.d_ctl;
+    a.n_multi_units = t.n_multi_units;
+    const dim3 block(Q_BLOCK);
+    const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
+    if (a.amax != nullptr) {
+        hipLaunchKernelGGL((k_quantize<TIn, Q_SLOTS, Q_BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    constexpr auto coop = k_quantize_coop<TIn, Q_SLOTS, Q_BLOCK, MUL>;
+    const int64_t resident = resident_groups<coop>(Q_BLOCK);
+    if (resident >= t.max_count) {
+        const int64_t work = static_cast<int64_t>(a.W) * t.n_tiles;
+        return launch_coop(coop, work < resident ? work : resident, Q_BLOCK, a, s);
+    }
+    // a unit with more tiles than resident work groups: two launches
+    QArgs p = a;
+    p.list = t.d_multi;
+    hipLaunchKernelGGL((k_tile_absmax<TIn, Q_SLOTS, Q_BLOCK>),
+                       dim3(static_cast<unsigned>(t.n_multi), static_cast<unsigned>(a.W)), block, 0, s, p);
+    hipLaunchKernelGGL((k_quantize<TIn, Q_SLOTS, Q_BLOCK, MUL, Q_FUSED>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// ---- launchers ----------------------------------------------------------------------------
+
+hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream_t s) {
+    QArgs a = a0;
+    a.list = nullptr;
+    a.partial = t.d_partial;
+    a.unit_first = t.d_unit_first;
+    a.tiles = t.d_tiles;
+    const bool mul = a.in_mul != 1.0f;
+    const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
+    const int64_t total = static_cast<int64_t>(a.W) * a.n_units;
+    const unsigned nb = static_cast<unsigned>((total + 255) / 256);
+    if (dt == GQ_F32) {
+        hipLaunchKernelGGL((k_tile_absmax<float, Q_SLOTS, Q_BLOCK>), grid, dim3(Q_BLOCK), 0, s, a);
+        hipLaunchKernelGGL(k_absmax_finalize<float>, dim3(nb), dim3(256), 0, s, a, mul);
+    } else {
+        hipLaunchKernelGGL((k_tile_absmax<__half, Q_SLOTS, Q_BLOCK>), grid, dim3(Q_BLOCK), 0, s, a);
+        hipLaunchKernelGGL(k_absmax_finalize<__half>, dim3(nb), dim3(256), 0, s, a, mul);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s) {
+    const bool mul = a.in_mul != 1.0f;
+    if (dt == GQ_F32)
+        return mul ? quantize_typed<float, true>(a, t, s) : quantize_typed<float, false>(a, t, s);
+    return mul ? quantize_typed<__half, true>(a, t, s) : quantize_typed<__half, false>(a, t, s);
+}
+
+hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipStream_t s) {
+    RArgs a = a0;
+    a.tiles = t.d_tiles;
+    a.partial = t.d_partial;
+    a.n_tiles = t.n_tiles;
+    a.pub = t.d_pub;
+    a.res = t.d_res;
+    a.cnt = t.d_cnt;
+    a.ctl = t.d_ctl;
+    const dim3 block(R_BLOCK);
+    if (!requantize) {
+        a.list = nullptr;
+        hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
+                           block, 0, s, a);
+        return hipGetLastError();
+    }
+    constexpr auto coop = k_reduce_coop<R_SLOTS, R_BLOCK>;
+    const int64_t resident = resident_groups<coop>(R_BLOCK);
+    if (resident >= t.max_count) {
+        return launch_coop(coop, t.n_tiles < resident ? t.n_tiles : resident, R_BLOCK, a, s);
+    }
+    RArgs p = a;
+    p.list = t.d_multi;
+    hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_PASS1>), dim3(static_cast<unsigned>(t.n_multi)),
+                       block, 0, s, p);
+    a.list = nullptr;
+    hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
+                       block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gq

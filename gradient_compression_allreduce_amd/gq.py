@@ -1,0 +1,205 @@
+"""Thin Python binding of libgq.so (argument marshalling only).
+
+Every function has the name and the meaning of the C entry point declared in
+include/gq.h; tensors are torch tensors on the current HIP device, and the
+work is enqueued on torch's current stream unless a stream is given.  All
+arithmetic runs in the library's gfx950 kernels; if the library is missing
+the import fails (there is no fallback).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SO = os.path.join(HERE, "_lib", "libgq.so")
+
+GQ_OK, GQ_ERR_INVALID, GQ_ERR_ALIGN, GQ_ERR_CAPACITY, GQ_ERR_HIP, GQ_ERR_DEVICE = range(6)
+GQ_F32, GQ_F16 = 0, 1
+GQ_MAX_RANKS = 64
+CHUNK_BYTES, ALIGN_BYTES = 131072, 64
+
+EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
+           "gq_units_destroy", "gq_units_info", "gq_units_faults", "gq_absmax", "gq_quantize",
+           "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize")
+
+
+class GQError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(SO):
+        raise ImportError("libgq.so is not built (%s); run __graft_entry__.build() or "
+                          "python gradient_compression_allreduce_amd/build.py" % SO)
+    L = ctypes.CDLL(SO)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    st = ctypes.c_int
+    L.gq_last_error.restype = ctypes.c_char_p
+    L.gq_last_error.argtypes = []
+    L.gq_version.restype = ctypes.c_char_p
+    L.gq_version.argtypes = []
+    L.gq_plan_chunks.restype = st
+    L.gq_plan_chunks.argtypes = [i64, i32, i64, i32, vp, i64, ctypes.POINTER(i64)]
+    L.gq_units_create.restype = st
+    L.gq_units_create.argtypes = [vp, i64, ctypes.POINTER(vp)]
+    L.gq_units_destroy.restype = st
+    L.gq_units_destroy.argtypes = [vp]
+    L.gq_units_info.restype = st
+    L.gq_units_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.gq_units_faults.restype = st
+    L.gq_units_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.gq_absmax.restype = st
+    L.gq_absmax.argtypes = [vp, i32, i32, f32, vp, vp, vp]
+    L.gq_quantize.restype = st
+    L.gq_quantize.argtypes = [vp, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.gq_reduce_dequant.restype = st
+    L.gq_reduce_dequant.argtypes = [vp, vp, i32, vp, vp, vp]
+    L.gq_requantize.restype = st
+    L.gq_requantize.argtypes = [vp, vp, vp, vp, vp]
+    L.gq_reduce_requantize.restype = st
+    L.gq_reduce_requantize.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+    return L
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != GQ_OK:
+        raise GQError(status, lib.gq_last_error().decode())
+
+
+def gq_last_error():
+    return lib.gq_last_error().decode()
+
+
+def gq_version():
+    return lib.gq_version().decode()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptrs(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return GQ_F32
+    if t.dtype == torch.float16:
+        return GQ_F16
+    raise TypeError("gradient elements must be float32 or float16, got %s" % t.dtype)
+
+
+def gq_plan_chunks(numel, elem_bytes, chunk_bytes=CHUNK_BYTES, align_bytes=ALIGN_BYTES):
+    """Chunk offsets (int64 numpy array of count+1 entries) of §2.1's
+    dynamic_chunk for a tensor of numel elements of elem_bytes each."""
+    cnt = ctypes.c_int64(0)
+    st = lib.gq_plan_chunks(numel, elem_bytes, chunk_bytes, align_bytes, None, 0,
+                            ctypes.byref(cnt))
+    if st != GQ_ERR_CAPACITY:
+        _check(st)
+    off = np.empty(cnt.value + 1, dtype=np.int64)
+    _check(lib.gq_plan_chunks(numel, elem_bytes, chunk_bytes, align_bytes,
+                              off.ctypes.data, off.size, ctypes.byref(cnt)))
+    return off
+
+
+class Units:
+    """Owner of a gq_units handle (destroyed with the object)."""
+
+    def __init__(self, offsets):
+        off = np.ascontiguousarray(offsets, dtype=np.int64)
+        h = ctypes.c_void_p()
+        _check(lib.gq_units_create(off.ctypes.data, off.size - 1, ctypes.byref(h)))
+        self.handle = h
+        self.offsets = off
+        self.n = int(off[-1])
+        self.n_units = off.size - 1
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+    def close(self):
+        if self.handle:
+            _check(lib.gq_units_destroy(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gq_units_create(offsets):
+    return Units(offsets)
+
+
+def gq_units_destroy(units):
+    units.close()
+
+
+def gq_units_info(units):
+    n, u = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.gq_units_info(units.handle, ctypes.byref(n), ctypes.byref(u)))
+    return n.value, u.value
+
+
+def gq_units_faults(units):
+    """Bounded waits that gave up on this table (synchronizes; 0 expected)."""
+    c = ctypes.c_uint64(0)
+    _check(lib.gq_units_faults(units.handle, ctypes.byref(c)))
+    return c.value
+
+
+def gq_absmax(xs, units, amax_bits, in_mul=1.0, stream=None):
+    """amax_bits: int32/uint32 tensor of W*n_units (rank-major), overwritten
+    with the bit patterns of max|x*in_mul| per unit."""
+    px, keep = _ptrs(xs)
+    _check(lib.gq_absmax(px, len(xs), _dtype_code(xs[0]), in_mul, units.handle,
+                         amax_bits.data_ptr(), _stream(stream)))
+
+
+def gq_quantize(xs, units, scales, codes, in_mul=1.0, amax_bits=None, stream=None):
+    """Per-unit scales (float32, n_units each) and int8 codes (n each) of W
+    gradients xs."""
+    px, k1 = _ptrs(xs)
+    ps, k2 = _ptrs(scales)
+    pq, k3 = _ptrs(codes)
+    am = amax_bits.data_ptr() if amax_bits is not None else None
+    _check(lib.gq_quantize(px, len(xs), _dtype_code(xs[0]), in_mul, units.handle, am,
+                           ps, pq, _stream(stream)))
+
+
+def gq_reduce_dequant(codes, scales, units, r_out, stream=None):
+    pq, k1 = _ptrs(codes)
+    ps, k2 = _ptrs(scales)
+    _check(lib.gq_reduce_dequant(pq, ps, len(codes), units.handle, r_out.data_ptr(),
+                                 _stream(stream)))
+
+
+def gq_requantize(r, units, scale_out, q_out, stream=None):
+    _check(lib.gq_requantize(r.data_ptr(), units.handle, scale_out.data_ptr(),
+                             q_out.data_ptr(), _stream(stream)))
+
+
+def gq_reduce_requantize(codes, scales, units, scale_out, q_out, r_out=None, stream=None):
+    pq, k1 = _ptrs(codes)
+    ps, k2 = _ptrs(scales)
+    rp = r_out.data_ptr() if r_out is not None else None
+    _check(lib.gq_reduce_requantize(pq, ps, len(codes), units.handle, rp,
+                                    scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))

@@ -1,0 +1,200 @@
+/*
+ * gq.h -- C ABI of libgq.so: the per-device compute of an INT8-compressed
+ * gradient AllReduce on AMD Instinct MI355X (gfx950).
+ *
+ * The method comes from the pipelined HCCL AllReduce article
+ * (bjdmk.com.cn/news/6235379):
+ *   §2.1   each gradient is cut into chunks by dynamic_chunk: a chunk count
+ *          of max(1, nbytes // (128 KiB rounded down to a 64-byte multiple))
+ *          and the pieces of torch.chunk;
+ *   §2.2.1 quantize_gradient: scale = max|g| / 127 and int8 codes
+ *          clamp(round(g / scale), -128, 127); the codes and the scale are
+ *          what an INT8 AllReduce exchanges;
+ *   §6.1   a loss-scaled fp16 gradient is unscaled before quantizing.
+ * The article does not define the INT8 AllReduce's arithmetic.  This library
+ * implements its reduction step on one device as: dequantize every rank's
+ * codes with that rank's scale, add the W contributions in fp32 in rank
+ * order 0..W-1 (a rounded multiply, then a rounded add; never a fused
+ * multiply-add), and quantize the sum again with a fresh absmax scale.  A
+ * unit whose maximum is 0 (or whose scale rounds to 0) gets scale 0 and all
+ * codes 0; a NaN quotient (a unit holding inf or NaN) gives code 0.
+ *
+ * "Units" are the element ranges that share one scale: a whole tensor, one
+ * layer tensor of a flattened bucket, or one chunk of a chunk plan.  W ranks
+ * of a data-parallel job are W separate buffers in this device's memory,
+ * all sharing one unit table (the same model on every rank).
+ *
+ * Conventions for every function below:
+ *   - Returns GQ_OK (0) or an error code; gq_last_error() then describes the
+ *     failure (operation, argument, reason) for the calling thread.
+ *   - Arguments are checked before anything is enqueued: an error return
+ *     means no work was launched and no output was touched.
+ *   - Device pointers must point to memory of the device that was current
+ *     when the unit table was created, and that device must be current at
+ *     the call.  Element buffers (inputs, codes, sums) must be 16-byte
+ *     aligned; scale and max buffers 4-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously: outputs are valid once the stream has reached
+ *     that point.  Nothing here synchronizes except gq_units_create/destroy.
+ *   - Buffers are owned by the caller and only borrowed while the enqueued
+ *     work runs.  The library never allocates in the compute calls.
+ *   - A unit table holds scratch memory: calls that use the same table must
+ *     be ordered (same stream, or ordered by events); calls on different
+ *     tables may overlap.
+ *   - Non-finite inputs follow IEEE arithmetic (see above); there is no
+ *     error for them.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQ_OK = 0,
+    GQ_ERR_INVALID = 1,  /* null pointer, bad size, bad unit table, W out of range */
+    GQ_ERR_ALIGN = 2,    /* a pointer is not aligned as required */
+    GQ_ERR_CAPACITY = 3, /* an output array is too small (plan query) */
+    GQ_ERR_HIP = 4,      /* the HIP runtime reported an error (launch, alloc) */
+    GQ_ERR_DEVICE = 5    /* wrong current device for this unit table */
+} gq_status;
+
+typedef enum {
+    GQ_F32 = 0, /* IEEE binary32 gradient elements */
+    GQ_F16 = 1  /* IEEE binary16 gradient elements (loss-scaled, see in_mul) */
+} gq_dtype;
+
+/* Largest number of simulated ranks a call accepts. */
+#define GQ_MAX_RANKS 64
+
+/* A hipStream_t, passed as an opaque pointer. */
+typedef void *gq_stream;
+
+/* Opaque unit table (host copy + device-resident work tables and scratch). */
+typedef struct gq_units gq_units;
+
+/* Description of the last error on the calling thread ("" if none). */
+const char *gq_last_error(void);
+
+/* Library version string. */
+const char *gq_version(void);
+
+/*
+ * gq_plan_chunks -- §2.1 dynamic_chunk, host only (no GPU needed).
+ *   k = max(1, numel*elem_bytes // (chunk_bytes - chunk_bytes % align_bytes))
+ *   pieces = torch.chunk(tensor, k): ceil(numel/k) elements each, the last
+ *   one shorter; count = ceil(numel / ceil(numel/k)) (equal to k unless
+ *   k*(k-1) >= numel).
+ * off_out  host array receiving count+1 element offsets (off[0] = 0,
+ *          off[count] = numel); may be NULL when cap = 0 (size query).
+ * cap      capacity of off_out in elements.
+ * count_out receives the number of pieces (also on GQ_ERR_CAPACITY).
+ * The article's constants are chunk_bytes = 131072 and align_bytes = 64.
+ * Errors: GQ_ERR_INVALID (numel < 1, elem_bytes < 1, chunk or alignment
+ * < 1, chunk_bytes rounded down to the alignment is 0, count_out NULL);
+ * GQ_ERR_CAPACITY (cap < count + 1; nothing written to off_out).
+ */
+gq_status gq_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
+                         int32_t align_bytes, int64_t *off_out, int64_t cap,
+                         int64_t *count_out);
+
+/*
+ * gq_units_create -- build a unit table on the current device.
+ * h_off    host array of n_units+1 element offsets: h_off[0] = 0, strictly
+ *          increasing; n = h_off[n_units] elements per rank (1 .. 2^40).
+ *          Unit u is [h_off[u], h_off[u+1]).  Units may start at any
+ *          element offset.  Per-tensor units are the tensors' boundaries in
+ *          the flat buffer; per-chunk units concatenate each tensor's
+ *          gq_plan_chunks offsets.
+ * out      receives the table.
+ * Allocates device memory (work tables + scratch, about 1 KiB per 32K
+ * elements) and synchronizes the device.  Errors: GQ_ERR_INVALID,
+ * GQ_ERR_HIP (allocation or copy failed).
+ */
+gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out);
+
+/* Free a unit table.  The work that uses it must have completed.  NULL is
+ * accepted.  Errors: GQ_ERR_HIP. */
+gq_status gq_units_destroy(gq_units *u);
+
+/* Elements per rank and number of units of a table. */
+gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
+
+/*
+ * gq_units_faults -- number of bounded waits that gave up since the table
+ * was created (0 unless the device failed to keep the cooperative work
+ * groups of a launch resident; the results of such a launch are invalid).
+ * Synchronizes the device.  count: host pointer receiving the number.
+ */
+gq_status gq_units_faults(const gq_units *u, uint64_t *count);
+
+/*
+ * gq_absmax -- §2.2.1 max|g| per unit and rank, with g = float(x) * in_mul
+ * (§6.1 unscale; in_mul = 1 for fp32, 1/S for a loss-scaled fp16 gradient).
+ * x          host array of W device pointers; x[w] holds n elements of dt.
+ * W          1 .. GQ_MAX_RANKS.
+ * in_mul     finite, > 0.
+ * amax_bits  device array [W][n_units] (rank-major), overwritten with the
+ *            bit pattern of max|g| (sign cleared; unsigned order, so a NaN
+ *            in the unit wins over inf, inf over every finite value).
+ */
+gq_status gq_absmax(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                    const gq_units *u, uint32_t *amax_bits, gq_stream stream);
+
+/*
+ * gq_quantize -- §2.2.1 quantize_gradient for W ranks, one scale per unit.
+ * scale = fl32(max|g| / 127); code = clamp(round_half_even(fl32(g / scale)),
+ * -128, 127); scale 0 gives codes 0; a NaN quotient gives code 0.
+ * x          host array of W device pointers (n elements of dt each).
+ * amax_bits  NULL: the maxima are computed here (one fused pass for units
+ *            of up to 128 KiB, two passes above that).  Otherwise a device
+ *            array [W][n_units] from gq_absmax (or any caller-provided
+ *            maxima as bit patterns of non-negative floats).
+ * scale_out  host array of W device pointers, each receiving n_units fp32.
+ * q_out      host array of W device pointers, each receiving n int8 codes.
+ */
+gq_status gq_quantize(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                      const gq_units *u, const uint32_t *amax_bits,
+                      float *const *scale_out, int8_t *const *q_out,
+                      gq_stream stream);
+
+/*
+ * gq_reduce_dequant -- the INT8 AllReduce reduction of §2.2.1 on one device:
+ *   r[i] = (((+0 + q_0[i]*s_0[u]) + q_1[i]*s_1[u]) + ...) + q_{W-1}[i]*s_{W-1}[u]
+ * in binary32, each product and each sum rounded (no fused multiply-add),
+ * ranks in order, u the unit of element i.
+ * q          host array of W device pointers (n int8 codes each).
+ * scale      host array of W device pointers (n_units fp32 each).
+ * r_out      device array of n fp32.
+ */
+gq_status gq_reduce_dequant(const int8_t *const *q, const float *const *scale,
+                            int32_t W, const gq_units *u, float *r_out,
+                            gq_stream stream);
+
+/*
+ * gq_requantize -- quantize a reduced fp32 sum again with fresh per-unit
+ * scales (gq_quantize of r with W = 1, in_mul = 1).
+ * r          device array of n fp32.
+ * scale_out  device array of n_units fp32.  q_out: device array of n int8.
+ */
+gq_status gq_requantize(const float *r, const gq_units *u, float *scale_out,
+                        int8_t *q_out, gq_stream stream);
+
+/*
+ * gq_reduce_requantize -- gq_reduce_dequant followed by gq_requantize,
+ * fused: the sum stays on chip for units of up to 128 KiB of fp32 sum (it
+ * is recomputed from the codes in a second pass for larger units).
+ * Results are bit-identical to the two separate calls.
+ * r_out      NULL, or a device array of n fp32 that also receives the sum.
+ */
+gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale,
+                               int32_t W, const gq_units *u, float *r_out,
+                               float *scale_out, int8_t *q_out, gq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_H */

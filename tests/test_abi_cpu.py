@@ -1,0 +1,139 @@
+"""Host-side checks of libgq.so that need no GPU: the library loads, exports
+every entry point include/gq.h declares, plans chunks exactly as the oracle
+does, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "gq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def gq():
+    from gradient_compression_allreduce_amd import gq as mod
+    return mod
+
+
+def test_exports_every_declared_symbol(gq):
+    names = _declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(gq.lib, name), name
+    assert set(names) == set(gq.EXPORTS)
+
+
+def test_version(gq):
+    assert "gfx950" in gq.gq_version()
+
+
+def test_plan_matches_oracle(gq, oracle):
+    rng = np.random.default_rng(20)
+    sizes = list(range(1, 2000, 7)) + [int(v) for v in rng.integers(1, 1 << 31, 300)]
+    sizes += [32768, 65536, 65535, 65537, 1 << 28, 30522 * 1024, 2359296]
+    for e in (1, 2, 4, 8):
+        for n in sizes:
+            assert np.array_equal(gq.gq_plan_chunks(n, e), oracle.plan_chunks(n, e)), (n, e)
+    for chunk, align in [(1000, 64), (4096, 4096), (5000, 3), (131072, 100)]:
+        for n in sizes[:200]:
+            assert np.array_equal(gq.gq_plan_chunks(n, 4, chunk, align),
+                                  oracle.plan_chunks(n, 4, chunk, align)), (n, chunk, align)
+
+
+def test_plan_workload_chunk_counts(gq):
+    """Per-chunk unit counts of the chunked workloads."""
+    from datagen import get_workload
+    w3 = get_workload(3)
+    k3 = sum(len(gq.gq_plan_chunks(int(s), 2)) - 1 for s in w3.sizes)
+    assert k3 == 5352
+    assert sum(1 for s in w3.sizes if len(gq.gq_plan_chunks(int(s), 2)) == 2) == 244
+    assert len(gq.gq_plan_chunks(1 << 28, 4)) - 1 == 8192
+    assert len(gq.gq_plan_chunks(1 << 20, 4)) - 1 == 32
+    w5 = get_workload(5)
+    assert all(len(gq.gq_plan_chunks(int(s), 4)) == 2 for s in w5.sizes)
+
+
+def test_plan_errors(gq):
+    L = gq.lib
+    cnt = ctypes.c_int64(-1)
+    assert L.gq_plan_chunks(0, 4, 131072, 64, None, 0, ctypes.byref(cnt)) == gq.GQ_ERR_INVALID
+    assert "numel" in gq.gq_last_error()
+    assert L.gq_plan_chunks(10, 0, 131072, 64, None, 0, ctypes.byref(cnt)) == gq.GQ_ERR_INVALID
+    assert L.gq_plan_chunks(10, 4, 63, 64, None, 0, ctypes.byref(cnt)) == gq.GQ_ERR_INVALID
+    assert L.gq_plan_chunks(10, 4, 131072, 64, None, 0, None) == gq.GQ_ERR_INVALID
+    assert L.gq_plan_chunks(1 << 20, 4, 131072, 64, None, 0, ctypes.byref(cnt)) == gq.GQ_ERR_CAPACITY
+    assert cnt.value == 32
+    buf = np.full(40, -7, dtype=np.int64)
+    assert L.gq_plan_chunks(1 << 20, 4, 131072, 64, buf.ctypes.data, 32,
+                            ctypes.byref(cnt)) == gq.GQ_ERR_CAPACITY
+    assert np.all(buf == -7)  # nothing written on error
+    assert L.gq_plan_chunks(1 << 20, 4, 131072, 64, buf.ctypes.data, 33,
+                            ctypes.byref(cnt)) == gq.GQ_OK
+    assert gq.gq_last_error() == ""
+
+
+def _arr(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def test_argument_errors_before_any_device_call(gq):
+    """Bad arguments are rejected on the host, before the unit table (and so
+    the device) is looked at: these run without a GPU."""
+    L = gq.lib
+    good = 0x10000
+    x = _arr([good] * 4)
+    s = _arr([good] * 4)
+    q = _arr([good] * 4)
+    null = None
+    # W out of range
+    assert L.gq_quantize(x, 0, gq.GQ_F32, 1.0, null, null, s, q, null) == gq.GQ_ERR_INVALID
+    assert L.gq_quantize(x, 65, gq.GQ_F32, 1.0, null, null, s, q, null) == gq.GQ_ERR_INVALID
+    # dtype / in_mul
+    assert L.gq_quantize(x, 4, 7, 1.0, null, null, s, q, null) == gq.GQ_ERR_INVALID
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.gq_quantize(x, 4, gq.GQ_F32, bad, null, null, s, q, null) == gq.GQ_ERR_INVALID
+    # null / misaligned pointers
+    assert L.gq_quantize(_arr([good, 0, good, good]), 4, gq.GQ_F32, 1.0, null, null, s, q,
+                         null) == gq.GQ_ERR_INVALID
+    assert "x[1]" in gq.gq_last_error()
+    assert L.gq_quantize(_arr([good, good + 4, good, good]), 4, gq.GQ_F32, 1.0, null, null,
+                         s, q, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_quantize(x, 4, gq.GQ_F32, 1.0, null, null, s, _arr([good] * 3 + [good + 8]),
+                         null) == gq.GQ_ERR_ALIGN
+    assert L.gq_quantize(x, 4, gq.GQ_F32, 1.0, null, good + 2, s, q, null) == gq.GQ_ERR_ALIGN
+    # everything fine except the unit table
+    assert L.gq_quantize(x, 4, gq.GQ_F32, 1.0, null, null, s, q, null) == gq.GQ_ERR_INVALID
+    assert "unit table" in gq.gq_last_error()
+    assert L.gq_absmax(x, 4, gq.GQ_F16, 2.0 ** -16, null, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_absmax(x, 4, gq.GQ_F16, 2.0 ** -16, null, null, null) == gq.GQ_ERR_INVALID
+    assert L.gq_reduce_dequant(q, s, 4, null, good + 4, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_reduce_dequant(q, s, 4, null, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_reduce_dequant(q, _arr([good, good + 2, good, good]), 4, null, good,
+                               null) == gq.GQ_ERR_ALIGN
+    assert L.gq_requantize(good, null, good, good + 1, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_requantize(null, null, good, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_reduce_requantize(q, s, 4, null, null, good, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_reduce_requantize(q, s, 4, null, good + 4, good, good, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_reduce_requantize(q, s, 0, null, null, good, good, null) == gq.GQ_ERR_INVALID
+
+
+def test_units_create_rejects_bad_tables(gq):
+    L = gq.lib
+    h = ctypes.c_void_p()
+    for off in ([0], [1, 5], [0, 5, 5], [0, 5, 3]):
+        a = np.array(off, dtype=np.int64)
+        st = L.gq_units_create(a.ctypes.data, a.size - 1, ctypes.byref(h))
+        assert st == gq.GQ_ERR_INVALID, off
+        assert not h.value
+    assert L.gq_units_create(None, 1, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert L.gq_units_destroy(None) == gq.GQ_OK

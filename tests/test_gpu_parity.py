@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element, bit-exact (NaN compared by NaN-ness).
+
+Sizes are small enough for the oracle to finish in seconds but span many
+work-group tiles, units longer than one tile (two-pass path), units at every
+offset modulo the 16-byte slot, and ragged tails."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import F16, F32, GpuStep, compare_step, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from gradient_compression_allreduce_amd import gq as mod
+    return mod
+
+
+def _offsets(rng, n, lo, hi):
+    cuts = [0]
+    while cuts[-1] < n:
+        cuts.append(min(n, cuts[-1] + int(rng.integers(lo, hi))))
+    return np.array(cuts, dtype=np.int64)
+
+
+def _grad(rng, n, kind):
+    sig = 10.0 ** rng.uniform(-5, -1)
+    g = rng.standard_normal(n) * sig
+    g[rng.random(n) < 0.03] = 0.0
+    if kind == F16:
+        return (g * 65536.0).astype(np.float16).view(np.uint16)
+    return g.astype(np.float32)
+
+
+def _run_and_compare(gq, oracle, xs, kind, off, in_mul, label, modes=("fused", "two_step")):
+    W = len(xs)
+    n = int(off[-1])
+    want = oracle.allreduce_step(xs, kind, off, in_mul)
+    dx = [to_device(x) for x in xs]
+    step = GpuStep(gq, off, W, kind, n)
+    for mode in modes:
+        say("case", label, "mode", mode, "W", W, "n", n, "units", len(off) - 1)
+        step.quantize(dx, in_mul, two_step=(mode == "two_step"))
+        step.reduce(fused=(mode == "fused"), with_r=True)
+        got = step.host()
+        compare_step(got, want, W, check_r=True, check_amax=(mode == "two_step"),
+                     label="%s/%s" % (label, mode))
+    # the benchmark's launch shape: fused quantize, fused reduce without r
+    step.quantize(dx, in_mul)
+    step.reduce(fused=True, with_r=False)
+    got = step.host()
+    compare_step(got, want, W, check_r=False, label=label + "/no_r")
+    return step
+
+
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_random_units_mixed_sizes(gq, oracle, kind, W):
+    """Units from 1 element to above two tiles, random offsets."""
+    rng = np.random.default_rng(100 + W + 10 * kind)
+    n = 400_003
+    off = _offsets(rng, n, 1, 150_000)
+    # sprinkle short units
+    extra = _offsets(rng, 5000, 1, 40) + n
+    off = np.concatenate([off, extra[1:]])
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(W)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "random_W%d_k%d" % (W, kind))
+
+
+def test_every_start_offset_mod_16(gq, oracle):
+    """Units of lengths 1..40 starting at every element offset modulo 16
+    (slot heads and tails), plus one unit of exactly one tile."""
+    rng = np.random.default_rng(7)
+    lens = []
+    for start_mod in range(16):
+        lens += [start_mod + 1, 16, 17, 31 + start_mod, 33]
+    lens += [32768, 32768 * 2 + 5, 65536, 3]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    for kind in (F32, F16):
+        xs = [_grad(rng, n, kind) for _ in range(4)]
+        in_mul = 2.0 ** -16 if kind == F16 else 1.0
+        _run_and_compare(gq, oracle, xs, kind, off, in_mul, "offsets_k%d" % kind)
+
+
+def test_single_element(gq, oracle):
+    for kind in (F32, F16):
+        rng = np.random.default_rng(3)
+        xs = [_grad(rng, 1, kind) for _ in range(2)]
+        off = np.array([0, 1], dtype=np.int64)
+        _run_and_compare(gq, oracle, xs, kind, off, 2.0 ** -16 if kind == F16 else 1.0,
+                         "n1_k%d" % kind)
+
+
+def test_zero_subnormal_and_overflow_units(gq, oracle):
+    """All-zero units (scale 0 -> codes 0), subnormal maxima on both sides
+    of the scale rounding to 0, sums overflowing to inf in rank order, and
+    units holding inf or NaN."""
+    tiny = np.float32(2.0 ** -149)
+    units = []
+    units.append(np.zeros(37, np.float32))
+    units.append(np.zeros(40000, np.float32))                # multi-tile zero unit
+    for k in (1, 63, 64, 100, 190, 8388607):
+        u = np.array([k, -k, 3, 0, -1] * 7, dtype=np.float32) * tiny
+        units.append(u)
+    big = np.full(50, 3.0e38, dtype=np.float32)
+    big[::2] *= -1
+    units.append(big)
+    units.append(np.array([1.0, np.inf, -2.0], np.float32))
+    units.append(np.array([1.0, np.nan, -2.0, 0.5], np.float32))
+    units.append(np.array([-np.inf], np.float32))
+    rng = np.random.default_rng(5)
+    units.append(rng.standard_normal(70000).astype(np.float32))  # multi-tile normal unit
+    x0 = np.concatenate(units)
+    off = np.concatenate([[0], np.cumsum([u.size for u in units])]).astype(np.int64)
+    n = int(off[-1])
+    xs = [x0.copy(), x0[::-1].copy(), (x0 * np.float32(0.5)).astype(np.float32),
+          x0.copy()]
+    _run_and_compare(gq, oracle, xs, F32, off, 1.0, "edge_values")
+
+
+def test_fp16_every_bit_pattern(gq, oracle):
+    """Every binary16 pattern (subnormals, inf and NaN included) through
+    load + unscale, in units of several sizes."""
+    bits = np.arange(65536, dtype=np.uint16)
+    rng = np.random.default_rng(9)
+    x1 = bits[rng.permutation(65536)]
+    off = np.array([0, 1000, 1024, 33000, 40000, 65536], dtype=np.int64)
+    _run_and_compare(gq, oracle, [bits.copy(), x1], F16, off, 2.0 ** -16, "fp16_patterns")
+    # finite patterns only, unscale 1 and an inexact multiplier
+    fin = bits[np.isfinite(bits.view(np.float16))]
+    off = np.array([0, 5000, fin.size], dtype=np.int64)
+    _run_and_compare(gq, oracle, [fin.copy(), fin[::-1].copy()], F16, off, 1.0, "fp16_mul1")
+    _run_and_compare(gq, oracle, [fin.copy()], F16, off, 0.1, "fp16_mul_0.1")
+
+
+def test_fp32_inexact_multiplier(gq, oracle):
+    rng = np.random.default_rng(11)
+    n = 100_000
+    off = _offsets(rng, n, 1, 50_000)
+    xs = [_grad(rng, n, F32) for _ in range(3)]
+    _run_and_compare(gq, oracle, xs, F32, off, 0.3, "f32_mul")
+
+
+@pytest.mark.parametrize("W", [2, 16, 64])
+def test_rank_counts(gq, oracle, W):
+    rng = np.random.default_rng(200 + W)
+    n = 70_001
+    off = _offsets(rng, n, 1000, 40_000)
+    xs = [_grad(rng, n, F32) for _ in range(W)]
+    _run_and_compare(gq, oracle, xs, F32, off, 1.0, "ranks_%d" % W, modes=("fused",))
+
+
+def test_half_integer_quotients(gq, oracle):
+    """Quotients exactly on k + 1/2 (ties to even) and one ulp either side."""
+    k = np.arange(-127, 127, dtype=np.float64)
+    base = (k + 0.5) * 2.0 ** -10
+    vals = np.concatenate([base, np.nextafter(base.astype(np.float32), np.float32(1)),
+                           np.nextafter(base.astype(np.float32), np.float32(-1)),
+                           [127 * 2.0 ** -10]]).astype(np.float32)
+    x = np.tile(vals, 40)
+    off = np.array([0, vals.size, 5 * vals.size, x.size], dtype=np.int64)
+    _run_and_compare(gq, oracle, [x, -x, x[::-1].copy()], F32, off, 1.0, "ties")
+
+
+def test_reuse_unit_table_and_outputs(gq, oracle):
+    """Two calls in a row on one table, the second with other values: no
+    state leaks between calls (scratch maxima are rewritten)."""
+    rng = np.random.default_rng(13)
+    n = 150_000
+    off = _offsets(rng, n, 20_000, 90_000)
+    xs1 = [_grad(rng, n, F32) * np.float32(100) for _ in range(4)]
+    xs2 = [_grad(rng, n, F32) for _ in range(4)]
+    step = GpuStep(gq, off, 4, F32, n)
+    for xs in (xs1, xs2):
+        want = oracle.allreduce_step(xs, F32, off)
+        step.quantize([to_device(x) for x in xs], 1.0)
+        step.reduce(fused=True, with_r=True)
+        compare_step(step.host(), want, 4, label="reuse")
+
+
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+def test_unit_larger_than_resident_groups(gq, oracle, kind):
+    """A unit of 12 M elements has more tiles than the device keeps resident
+    work groups, so the quantize and the reduce take the two-launch path;
+    small units around it keep the one-launch path's shapes."""
+    rng = np.random.default_rng(21 + kind)
+    lens = [1000, 12_000_003, 70_000, 5]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(2)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "big_unit_k%d" % kind,
+                     modes=("fused",))
+
+
+def test_errors_on_device(gq):
+    """Argument errors reported by the ABI leave outputs untouched."""
+    import torch
+    off = np.array([0, 100], dtype=np.int64)
+    units = gq.gq_units_create(off)
+    x = torch.zeros(100, device="cuda")
+    s = torch.full((1,), 7.0, device="cuda")
+    q = torch.full((100,), 5, dtype=torch.int8, device="cuda")
+    with pytest.raises(gq.GQError) as e:
+        gq.gq_quantize([x], units, [s], [q], in_mul=-1.0)
+    assert e.value.status == gq.GQ_ERR_INVALID
+    with pytest.raises(gq.GQError) as e:
+        gq.gq_quantize([x[1:]], units, [s], [q])
+    assert e.value.status == gq.GQ_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert float(s[0]) == 7.0 and int(q[0]) == 5
+    n, U = gq.gq_units_info(units)
+    assert (n, U) == (100, 1)

@@ -9,7 +9,7 @@ import os
 import pytest
 
 import oracle as oracle_pkg
-import pins
+from tests import pins
 
 # (name, original text, mutated text); each original must occur exactly once
 MUTANTS = [

@@ -2,7 +2,7 @@
 routines, hand-worked examples): runs without a GPU."""
 import pytest
 
-import pins
+from tests import pins
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
