@@ -8,4 +8,4 @@ from . import gq  # noqa: F401
 from .gq import (  # noqa: F401
     GQError, Units, gq_absmax, gq_last_error, gq_plan_chunks, gq_quantize,
     gq_reduce_dequant, gq_reduce_requantize, gq_requantize, gq_units_create,
-    gq_units_destroy, gq_units_faults, gq_units_info, gq_version)
+    gq_units_destroy, gq_units_faults, gq_units_info, gq_units_schedule, gq_version)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -77,6 +78,8 @@ hipError_t upload(T **dst, const std::vector<T> &src) {
 
 void free_table(gq::Table &t) {
     if (t.d_tiles) (void)hipFree(t.d_tiles);
+    if (t.d_small) (void)hipFree(t.d_small);
+    if (t.d_big) (void)hipFree(t.d_big);
     if (t.d_multi) (void)hipFree(t.d_multi);
     if (t.d_partial) (void)hipFree(t.d_partial);
     if (t.d_unit_first) (void)hipFree(t.d_unit_first);
@@ -200,24 +203,67 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
     hipError_t e = hipMalloc(reinterpret_cast<void **>(&U->d_faults), sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(U->d_faults, 0, sizeof(uint32_t));
     for (int ti = 0; ti < gq::TAB_COUNT && e == hipSuccess; ++ti) {
-        const gq::TableGeom g = gq::kGeom[ti];
+        const int V = gq::kSlotElems[ti];
+        gq::Table &t = U->tab[ti];
+        const int64_t small_cap =
+            64 * static_cast<int64_t>(ti == gq::TAB_R ? gq::SMALL_SLOTS_R : gq::SMALL_SLOTS_Q);
+        auto span = [&](int64_t u) { return (off[u + 1] + V - 1) / V - off[u] / V; };
+        if (ti == gq::TAB_R) {
+            t.sched = gq::SCHED_LAYER;
+            t.block = gq::R_BLOCK;
+            t.slots = gq::R_SLOTS;
+        } else {
+            // chunk schedule when most elements of the non-small units sit
+            // in units of one chunk tile
+            const int64_t cap = static_cast<int64_t>(gq::Q_BLOCK_CHUNK) * gq::Q_SLOTS_CHUNK;
+            int64_t in_single = 0, in_big = 0;
+            for (int64_t u = 0; u < n_units; ++u) {
+                if (span(u) <= small_cap) continue;
+                in_big += off[u + 1] - off[u];
+                if (span(u) <= cap) in_single += off[u + 1] - off[u];
+            }
+            t.sched = (2 * in_single >= in_big) ? gq::SCHED_CHUNK : gq::SCHED_LAYER;
+            t.block = t.sched == gq::SCHED_CHUNK ? gq::Q_BLOCK_CHUNK : gq::Q_BLOCK_LAYER;
+            t.slots = t.sched == gq::SCHED_CHUNK ? gq::Q_SLOTS_CHUNK : gq::Q_SLOTS_LAYER;
+        }
         std::vector<gq::Tile> tiles;
         std::vector<int32_t> multi, unit_first;
-        gq::Table &t = U->tab[ti];
-        build_tiles(off, g.V, static_cast<int64_t>(g.block) * g.slots, tiles, multi, unit_first,
+        build_tiles(off, V, static_cast<int64_t>(t.block) * t.slots, tiles, multi, unit_first,
                     t.n_multi_units, t.max_count);
+        // hot-path split: small units, and the tiles of the others
+        std::vector<gq::Tile> small, big;
+        int32_t big_max = 1;
+        for (int64_t u = 0; u < n_units; ++u) {
+            if (span(u) <= small_cap) {
+                small.push_back({off[u], off[u + 1], static_cast<int32_t>(u),
+                                 static_cast<int32_t>(small.size()), 1, -1});
+                continue;
+            }
+            const int32_t first_big = static_cast<int32_t>(big.size());
+            for (int32_t k = unit_first[u]; k < unit_first[u + 1]; ++k) {
+                gq::Tile tl = tiles[k];
+                tl.first = first_big;
+                big.push_back(tl);
+            }
+            big_max = std::max(big_max, unit_first[u + 1] - unit_first[u]);
+        }
         t.n_tiles = static_cast<int64_t>(tiles.size());
         t.n_multi = static_cast<int64_t>(multi.size());
+        t.n_small = static_cast<int64_t>(small.size());
+        t.n_big = static_cast<int64_t>(big.size());
+        t.big_max_count = big_max;
         e = upload(&t.d_tiles, tiles);
         if (e == hipSuccess) e = upload(&t.d_multi, multi);
         if (e == hipSuccess) e = upload(&t.d_unit_first, unit_first);
+        if (e == hipSuccess) e = upload(&t.d_small, small);
+        if (e == hipSuccess) e = upload(&t.d_big, big);
         const size_t partial_bytes = sizeof(uint32_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_tiles);
         if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_partial), partial_bytes);
         if (e == hipSuccess) e = hipMemset(t.d_partial, 0, partial_bytes);
         if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t.d_ctl), 4 * sizeof(uint32_t));
         if (e == hipSuccess) e = hipMemset(t.d_ctl, 0, 4 * sizeof(uint32_t));
         if (e == hipSuccess && t.n_multi_units > 0) {
-            const size_t pub_bytes = sizeof(uint64_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_tiles);
+            const size_t pub_bytes = sizeof(uint64_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_big);
             const size_t unit_bytes =
                 sizeof(uint64_t) * GQ_MAX_RANKS * static_cast<size_t>(t.n_multi_units);
             e = hipMalloc(reinterpret_cast<void **>(&t.d_pub), pub_bytes);
@@ -232,6 +278,12 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
         (void)gq_units_destroy(U);
         return fail(GQ_ERR_HIP, op, "device allocation failed: %s", hipGetErrorString(e));
     }
+    for (int ti = 0; ti < gq::TAB_COUNT; ++ti) {
+        if (!gq::table_ready(U->tab[ti], n_units)) {
+            (void)gq_units_destroy(U);
+            return fail(GQ_ERR_HIP, op, "internal error: work table %d incomplete", ti);
+        }
+    }
     if (hipDeviceSynchronize() != hipSuccess) {
         (void)gq_units_destroy(U);
         return fail(GQ_ERR_HIP, op, "synchronize failed");
@@ -245,6 +297,15 @@ gq_status gq_units_destroy(gq_units *u) {
     for (int k = 0; k < gq::TAB_COUNT; ++k) free_table(u->tab[k]);
     if (u->d_faults) (void)hipFree(u->d_faults);
     delete u;
+    return ok();
+}
+
+gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched) {
+    const char *op = "gq_units_schedule";
+    if (!u) return fail(GQ_ERR_INVALID, op, "unit table is NULL");
+    if (!sched) return fail(GQ_ERR_INVALID, op, "sched is NULL");
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    *sched = u->tab[q_table(dt)].sched;
     return ok();
 }
 

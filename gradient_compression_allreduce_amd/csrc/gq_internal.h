@@ -28,22 +28,33 @@ static_assert(sizeof(Tile) == 32, "Tile layout");
 // threads holds up to block * slots slots of a tile in registers.
 enum TableId { TAB_Q32 = 0, TAB_Q16 = 1, TAB_R = 2, TAB_COUNT = 3 };
 
-struct TableGeom {
-    int V;       // elements per slot
-    int block;   // threads per work group
-    int slots;   // slots per thread
-};
+// Schedules of the persistent quantize kernel, chosen per unit table:
+//  SCHED_LAYER  units spanning many tiles (per-tensor or per-layer scales):
+//               512-thread tiles; a tile's max is published one tile ahead
+//               of the wait for its unit max, which leaves slack for the
+//               unit's other tiles to arrive.
+//  SCHED_CHUNK  units of about one tile (per-chunk scales, small tensors):
+//               1024-thread tiles of 144 KiB, which hold a whole chunk of
+//               the chunk plan for every tensor of 1 MiB or more (those
+//               chunks are below 128 KiB * 9/8); the next tile's loads are
+//               in flight while the current tile's codes are written.
+enum Sched { SCHED_LAYER = 0, SCHED_CHUNK = 1 };
 
-constexpr int Q_BLOCK = 512;
-constexpr int Q_SLOTS = 8;      // fp32: 8 x 4 = 32 elements per thread (16384 per tile)
+constexpr int Q_SLOTS_LAYER = 8;     // 8 x 16 bytes per thread
+constexpr int Q_SLOTS_CHUNK = 9;     // 9 x 16 bytes per thread
+constexpr int Q_BLOCK_LAYER = 512;   // fp32: 16384 elements per tile (64 KiB)
+constexpr int Q_BLOCK_CHUNK = 1024;  // fp32: 36864 elements per tile (144 KiB)
 constexpr int R_BLOCK = 512;
-constexpr int R_SLOTS = 1;      // 16 codes = 16 sums per thread (8192 per tile)
+constexpr int R_SLOTS = 1;           // 16 codes = 16 sums per thread (8192 per tile)
 
-constexpr TableGeom kGeom[TAB_COUNT] = {
-    {4, Q_BLOCK, Q_SLOTS},   // fp32 quantize / requantize
-    {8, Q_BLOCK, Q_SLOTS},   // fp16 quantize: 32768 elements per tile
-    {16, R_BLOCK, R_SLOTS},  // reduce
-};
+// Units whose 16-byte slots span at most 64 * SMALL_SLOTS[table] slots are
+// "small": one wave handles a whole unit in a plain (non-persistent) launch,
+// with no tile exchange and no ticket.
+constexpr int SMALL_BLOCK = 256;     // four waves, four units per work group
+constexpr int SMALL_SLOTS_Q = 16;    // fp32: 4096 elements, fp16: 8192 elements
+constexpr int SMALL_SLOTS_R = 4;     // 4096 elements
+
+constexpr int kSlotElems[TAB_COUNT] = {4, 8, 16};  // V of each table
 
 // Cross-work-group state of the persistent kernels: one published-max word
 // per tile and rank and one result word per multi-tile unit and rank (high
@@ -53,19 +64,39 @@ constexpr TableGeom kGeom[TAB_COUNT] = {
 // groups}.
 
 struct Table {
+    int sched = SCHED_LAYER;
+    int block = 0;                  // threads per work group
+    int slots = 0;                  // slots per thread
     int64_t n_tiles = 0;
     int64_t n_multi = 0;            // tiles of multi-tile units
     int64_t n_multi_units = 0;      // multi-tile units
     int32_t max_count = 1;          // largest tile count of one unit
-    Tile *d_tiles = nullptr;        // [n_tiles], unit order
+    Tile *d_tiles = nullptr;        // [n_tiles], every unit, unit order
+    int64_t n_small = 0;            // small units
+    Tile *d_small = nullptr;        // [n_small] one entry per small unit
+    int64_t n_big = 0;              // tiles of the other units
+    Tile *d_big = nullptr;          // [n_big], unit order (first: index into d_big)
+    int32_t big_max_count = 1;      // largest tile count of a unit in d_big
     int32_t *d_multi = nullptr;     // [n_multi] indices of multi tiles
     uint32_t *d_partial = nullptr;  // [GQ_MAX_RANKS][n_tiles] per-tile maxima
     int32_t *d_unit_first = nullptr;  // [n_units+1] first tile of each unit
-    uint64_t *d_pub = nullptr;      // [GQ_MAX_RANKS][n_tiles] published tile maxima
+    uint64_t *d_pub = nullptr;      // [GQ_MAX_RANKS][n_big] published tile maxima
     uint64_t *d_res = nullptr;      // [GQ_MAX_RANKS][n_multi_units] published unit maxima
     uint64_t *d_cnt = nullptr;      // [GQ_MAX_RANKS][n_multi_units] arrivals
     uint32_t *d_ctl = nullptr;      // [4]: launch epoch, exited work groups, next ticket
 };
+
+// Every array a launcher may hand to a kernel is present and sized for the
+// table (launchers check this before launching anything).
+inline bool table_ready(const Table &t, int64_t n_units) {
+    if (t.n_tiles < n_units || !t.d_tiles || !t.d_unit_first || !t.d_partial || !t.d_ctl)
+        return false;
+    if (t.n_multi > 0 && !t.d_multi) return false;
+    if (t.n_small + t.n_big < 1 || (t.n_small > 0 && !t.d_small) || (t.n_big > 0 && !t.d_big))
+        return false;
+    if (t.n_multi_units > 0 && (!t.d_pub || !t.d_res || !t.d_cnt)) return false;
+    return t.block > 0 && t.slots > 0;
+}
 
 }  // namespace gq
 
@@ -86,11 +117,13 @@ struct QArgs {
     int8_t *q[GQ_MAX_RANKS];
     const Tile *tiles;
     const int32_t *list;        // NULL: blockIdx.x is the tile index
+    const Tile *small;          // small units (one wave each)
+    int64_t n_small;
     uint32_t *partial;          // [W][n_tiles]
     const uint32_t *amax;       // [W][n_units] or NULL
     const int32_t *unit_first;  // for the finalize step
     uint32_t *amax_out;         // [W][n_units] (gq_absmax)
-    uint64_t *pub;              // [W][n_tiles]
+    uint64_t *pub;              // [W][n_tiles of the tile list in use]
     uint64_t *res;              // [W][n_multi_units]
     uint64_t *cnt;              // [W][n_multi_units]
     uint32_t *ctl;              // [4]
@@ -108,6 +141,8 @@ struct RArgs {
     const float *scale[GQ_MAX_RANKS];
     const Tile *tiles;
     const int32_t *list;
+    const Tile *small;          // small units (one wave each)
+    int64_t n_small;
     uint32_t *partial;          // [n_tiles]
     float *r;                   // NULL or [n]
     float *scale_out;           // [n_units]

@@ -61,10 +61,12 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 // threadIdx.x as a value the compiler cannot see through, so that per-lane
 // index arithmetic is not hoisted out of the persistent loops (hoisted
 // values stay live across the whole loop and cost registers).
+// With GROUP == 64 one wave works on a tile alone: the lane index.
+template <int GROUP>
 __device__ __forceinline__ int64_t opaque_tid() {
     int v;
     asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(static_cast<int>(threadIdx.x)));
-    return v;
+    return GROUP == 64 ? (v & 63) : v;
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -105,6 +107,37 @@ __device__ __forceinline__ int code_fast(float g, float s, float r) {
     const float d = fabsf(__fsub_rn(q0, c));
     if (d >= kNearHalf) c = __builtin_rintf(__fdiv_rn(g, s));
     return static_cast<int>(c);
+}
+
+// Codes of four values in the fast mode (normal scale, |g| <= max), packed
+// into the four bytes of a word.  Adding 1.5 * 2^23 to q0 = fl(g * r)
+// rounds it to an integer half-to-even (|q0| < 2^22) and leaves that
+// integer, as a two's-complement byte, in the low byte of the sum; if any of
+// the four estimates lies within 2^-15 of a half-integer, the four codes
+// are redone with exact division (rare).
+__device__ __forceinline__ uint32_t codes4_fast(float g0, float g1, float g2, float g3, float s,
+                                                float r) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const float q0 = __fmul_rn(g0, r), q1 = __fmul_rn(g1, r);
+    const float q2 = __fmul_rn(g2, r), q3 = __fmul_rn(g3, r);
+    const float t0 = __fadd_rn(q0, kMagic), t1 = __fadd_rn(q1, kMagic);
+    const float t2 = __fadd_rn(q2, kMagic), t3 = __fadd_rn(q3, kMagic);
+    const float d0 = fabsf(__fsub_rn(q0, __fsub_rn(t0, kMagic)));
+    const float d1 = fabsf(__fsub_rn(q1, __fsub_rn(t1, kMagic)));
+    const float d2 = fabsf(__fsub_rn(q2, __fsub_rn(t2, kMagic)));
+    const float d3 = fabsf(__fsub_rn(q3, __fsub_rn(t3, kMagic)));
+    uint32_t b0 = __float_as_uint(t0), b1 = __float_as_uint(t1);
+    uint32_t b2 = __float_as_uint(t2), b3 = __float_as_uint(t3);
+    if (fmaxf(fmaxf(d0, d1), fmaxf(d2, d3)) >= kNearHalf) {
+        b0 = static_cast<uint32_t>(code_exact(g0, s));
+        b1 = static_cast<uint32_t>(code_exact(g1, s));
+        b2 = static_cast<uint32_t>(code_exact(g2, s));
+        b3 = static_cast<uint32_t>(code_exact(g3, s));
+    }
+    // low bytes of b0..b3 -> bytes 0..3 (selector 0x0c yields a zero byte)
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+    return lo | hi;
 }
 
 enum CodeMode { CM_ZERO = 0, CM_FAST = 1, CM_EXACT = 2 };
@@ -264,15 +297,19 @@ template <typename TIn, int S, int BLOCK>
 __device__ __forceinline__ void issue_tile(const void *x, const Tile &t, int64_t n,
                                            typename In<TIn>::Raw (&raw)[S]) {
     constexpr int V = In<TIn>::V;
-    const int64_t tid = opaque_tid();
-    const int64_t j0 = t.begin / V;
+    const int64_t tid = opaque_tid<BLOCK>();
+    const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
     const int64_t nfull = n / V;
+    // last slot to touch: the tile's last slot, at most the buffer's last
+    // whole slot (lanes past the tile all load that one address, which the
+    // memory pipeline merges)
+    const int64_t jmax = (j1 < nfull ? j1 : nfull) - 1;
     const uint4 *xv = static_cast<const uint4 *>(x);
-    if (nfull > 0) {
+    if (jmax >= 0) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-            raw[s] = xv[j < nfull ? j : nfull - 1];
+            raw[s] = xv[j < jmax ? j : jmax];
         }
     }
 }
@@ -283,7 +320,7 @@ template <typename TIn, int S, int BLOCK>
 __device__ __forceinline__ uint32_t fix_tile(const void *x, const Tile &t, int64_t n,
                                              typename In<TIn>::Raw (&raw)[S]) {
     constexpr int V = In<TIn>::V;
-    const int64_t tid = opaque_tid();
+    const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -342,26 +379,35 @@ __device__ __forceinline__ void quantize_tile_mode(const typename In<TIn>::Raw (
                                                    const Tile &t, float in_mul,
                                                    const QuantParams &p, int8_t *q) {
     constexpr int V = In<TIn>::V;
-    const int64_t tid = opaque_tid();
+    const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
         if (j >= j1) continue;
-        int c[V];
+        float g[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            float g = In<TIn>::elem(raw[s], k);
-            if (MUL) g = __fmul_rn(g, in_mul);
-            c[k] = code_of<MODE>(g, p);
+            g[k] = In<TIn>::elem(raw[s], k);
+            if (MUL) g[k] = __fmul_rn(g[k], in_mul);
+        }
+        uint32_t pk[V / 4];
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            if constexpr (MODE == CM_FAST) {
+                pk[k] = codes4_fast(g[4 * k], g[4 * k + 1], g[4 * k + 2], g[4 * k + 3], p.s, p.r);
+            } else {
+                pk[k] = pack4(code_of<MODE>(g[4 * k], p), code_of<MODE>(g[4 * k + 1], p),
+                              code_of<MODE>(g[4 * k + 2], p), code_of<MODE>(g[4 * k + 3], p));
+            }
         }
         const int64_t i0 = j * V;
         if constexpr (V == 4) {
-            const uint32_t p0 = pack4(c[0], c[1], c[2], c[3]);
+            const uint32_t p0 = pk[0];
             if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint32_t *>(q + i0) = p0;
             else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, 0, 0, 0));
         } else {
-            const uint32_t p0 = pack4(c[0], c[1], c[2], c[3]), p1 = pack4(c[4], c[5], c[6], c[7]);
+            const uint32_t p0 = pk[0], p1 = pk[1];
             if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint2 *>(q + i0) = make_uint2(p0, p1);
             else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, p1, 0, 0));
         }
@@ -494,14 +540,92 @@ __device__ __forceinline__ Tile load_desc(const Tile *tiles, int64_t i) {
 
 // ---- quantize kernels -------------------------------------------------------------
 
-// Hot path: every tile of every rank, one read of the input.  A work group
-// loads its next tile and publishes that tile's max before it waits for the
-// current tile's unit max, so that it never blocks while holding an
-// unpublished tile (see the scheduling note above) and the wait overlaps the
-// next tile's loads.
+// Hot path, SCHED_CHUNK: every tile of every rank, one read of the input.
+// Per tile, a work group: issues the loads of its next tile; writes the codes of its
+// current tile (whose unit max it already has), so the loads are in flight
+// during the code pass; takes the next tile's max, publishes it and waits
+// for that unit's max; then takes a new ticket.  It blocks only while
+// holding no unpublished tile and no untaken-but-unstarted ticket.
 template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
-void k_quantize_coop(const QArgs a) {
+void k_quantize_chunk(const QArgs a) {
+    using Raw = typename In<TIn>::Raw;
+    __shared__ uint32_t sh[BLOCK / 64];
+    __shared__ uint32_t s_val[2];  // unit max, ticket
+    const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
+    const uint32_t tag = launch_tag(a.ctl);
+    Raw cur[S], nxt[S];
+
+    // ticket -> (rank, tile index, descriptor)
+    auto next_ticket = [&]() -> int64_t {
+        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+        __syncthreads();
+        const int64_t t = s_val[1];
+        __syncthreads();
+        return t;
+    };
+    // max of a loaded tile, published and combined into its unit max
+    // (blocks until the unit is complete)
+    auto tile_max = [&](Raw (&buf)[S], const Tile &t, int w, int32_t tix) -> uint32_t {
+        uint32_t m = block_max<BLOCK>(fix_tile<TIn, S, BLOCK>(a.x[w], t, a.n, buf), sh);
+        if (t.count > 1) {
+            if (threadIdx.x < 64) {
+                uint64_t *pub = a.pub + static_cast<int64_t>(w) * a.n_tiles;
+                const int64_t u = static_cast<int64_t>(w) * a.n_multi_units + t.slot;
+                const uint64_t arr = unit_publish(pub, a.cnt + u, tix, m, tag);
+                const uint32_t um = unit_max(pub, a.res + u, tix, t.first, t.count, m, arr, tag,
+                                             a.faults);
+                if (threadIdx.x == 0) s_val[0] = um;
+            }
+            __syncthreads();
+            m = s_val[0];
+        }
+        return m;
+    };
+
+    int64_t tk = next_ticket();
+    if (tk < total) {
+        int wc = static_cast<int>(tk / a.n_tiles);
+        int32_t tix = static_cast<int32_t>(tk - static_cast<int64_t>(wc) * a.n_tiles);
+        Tile tc = load_desc(a.tiles, tix);
+        issue_tile<TIn, S, BLOCK>(a.x[wc], tc, a.n, cur);
+        uint32_t mc = tile_max(cur, tc, wc, tix);
+        int64_t tn = next_ticket();
+        for (;;) {
+            const bool more = tn < total;
+            int wn = 0;
+            int32_t tixn = 0;
+            Tile tnx{};
+            if (more) {
+                wn = static_cast<int>(tn / a.n_tiles);
+                tixn = static_cast<int32_t>(tn - static_cast<int64_t>(wn) * a.n_tiles);
+                tnx = load_desc(a.tiles, tixn);
+                issue_tile<TIn, S, BLOCK>(a.x[wn], tnx, a.n, nxt);
+            }
+            const float sc = __fdiv_rn(In<TIn>::max_value(mc, a.in_mul, MUL), 127.0f);
+            if (threadIdx.x == 0 && tix == tc.first) a.scale[wc][tc.unit] = sc;
+            quantize_tile<TIn, S, BLOCK, MUL>(cur, tc, a.in_mul, quant_params(sc, true), a.q[wc]);
+            if (!more) break;
+            mc = tile_max(nxt, tnx, wn, tixn);
+#pragma unroll
+            for (int s = 0; s < S; ++s) cur[s] = nxt[s];
+            tc = tnx;
+            wc = wn;
+            tix = tixn;
+            tn = next_ticket();
+        }
+    }
+    launch_exit(a.ctl);
+}
+
+// Hot path, SCHED_LAYER: every tile of every rank, one read of the input.
+// A work group loads its next tile and publishes that tile's max before it
+// waits for the current tile's unit max, so it never blocks while holding an
+// unpublished tile (see the scheduling note above), and a tile's max is
+// published a whole tile ahead of the wait for its unit.
+template <typename TIn, int S, int BLOCK, bool MUL>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void k_quantize_layer(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
@@ -568,6 +692,23 @@ void k_quantize_coop(const QArgs a) {
         arr_c = arr_n;
     }
     launch_exit(a.ctl);
+}
+
+// Small units: one wave per (rank, unit), four per work group, no tile
+// exchange and no ticket.
+template <typename TIn, int SS, bool MUL>
+__global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
+    using Raw = typename In<TIn>::Raw;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= static_cast<int64_t>(a.W) * a.n_small) return;
+    const int w = static_cast<int>(item / a.n_small);
+    const Tile t = a.small[item - static_cast<int64_t>(w) * a.n_small];
+    Raw raw[SS];
+    const uint32_t m = wave_max(load_tile<TIn, SS, 64>(a.x[w], t, a.n, raw));
+    const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
+    if ((threadIdx.x & 63) == 0) a.scale[w][t.unit] = sc;
+    quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
 }
 
 // Fallback pass 1 (and gq_absmax): per-tile max of the listed tiles.
@@ -650,9 +791,9 @@ __device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float 
 }
 
 // Rank-order dequant-accumulate of the S slots of tile t into acc.
-template <int S, int BLOCK>
+template <int S, int BLOCK, int RG = 4>
 __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float (&acc)[S][RV]) {
-    const int64_t tid = opaque_tid();
+    const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -665,11 +806,11 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
     // end are redone afterwards.  Whole 16-byte slots are read even where a
     // unit boundary cuts them (the bytes belong to the rank's buffer); sums
     // of elements outside the tile are cleared below.
-    constexpr int RG = 4;
     const int64_t nfull = a.n / RV;
+    const int64_t jmax = (j1 < nfull ? j1 : nfull) - 1;
     uint4 cur[RG][S], nxt[RG][S];
     auto issue = [&](int w0, uint4 (&v)[RG][S]) {
-        if (nfull <= 0) return;
+        if (jmax < 0) return;
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             if (w0 + r >= a.W) break;
@@ -677,7 +818,7 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-                v[r][s] = qv[j < nfull ? j : nfull - 1];
+                v[r][s] = qv[j < jmax ? j : jmax];
             }
         }
     };
@@ -732,7 +873,7 @@ __device__ __forceinline__ uint32_t acc_absmax(const float (&acc)[S][RV]) {
 
 template <int S, int BLOCK>
 __device__ __forceinline__ void store_sum(const Tile &t, const float (&acc)[S][RV], float *r) {
-    const int64_t tid = opaque_tid();
+    const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -756,18 +897,25 @@ __device__ __forceinline__ void store_sum(const Tile &t, const float (&acc)[S][R
 template <int S, int BLOCK, int MODE>
 __device__ __forceinline__ void requantize_tile_mode(const Tile &t, const float (&acc)[S][RV],
                                                      const QuantParams &p, int8_t *q) {
-    const int64_t tid = opaque_tid();
+    const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
         if (j >= j1) continue;
-        int c[RV];
+        uint32_t w4[4];
 #pragma unroll
-        for (int k = 0; k < RV; ++k) c[k] = code_of<MODE>(acc[s][k], p);
+        for (int k = 0; k < 4; ++k) {
+            const float *g = &acc[s][4 * k];
+            if constexpr (MODE == CM_FAST) {
+                w4[k] = codes4_fast(g[0], g[1], g[2], g[3], p.s, p.r);
+            } else {
+                w4[k] = pack4(code_of<MODE>(g[0], p), code_of<MODE>(g[1], p),
+                              code_of<MODE>(g[2], p), code_of<MODE>(g[3], p));
+            }
+        }
         const int64_t i0 = j * RV;
-        const uint4 pk = make_uint4(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]),
-                                    pack4(c[8], c[9], c[10], c[11]), pack4(c[12], c[13], c[14], c[15]));
+        const uint4 pk = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         if (i0 >= t.begin && i0 + RV <= t.end) *reinterpret_cast<uint4 *>(q + i0) = pk;
         else store_codes_part(q, i0, RV, t.begin, t.end, pk);
     }
@@ -855,6 +1003,22 @@ void k_reduce_coop(const RArgs a) {
     launch_exit(a.ctl);
 }
 
+// Small units: one wave per unit, four per work group.
+template <int SR>
+__global__ __launch_bounds__(SMALL_BLOCK) void k_reduce_small(const RArgs a) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= a.n_small) return;
+    const Tile t = a.small[item];
+    float acc[SR][RV];
+    reduce_tile<SR, 64, 1>(a, t, acc);
+    if (a.r) store_sum<SR, 64>(t, acc, a.r);
+    const uint32_t m = wave_max(acc_absmax<SR>(acc));
+    const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+    if ((threadIdx.x & 63) == 0) a.scale_out[t.unit] = sc;
+    requantize_tile<SR, 64>(t, acc, quant_params(sc, true), a.q_out);
+}
+
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
 
 // Non-persistent reduce: the plain sum (R_SUM), and the two-launch fallback
@@ -932,6 +1096,52 @@ hipError_t launch_coop(K kernel, int64_t groups, int block, const A &args, hipSt
                                       dim3(static_cast<unsigned>(groups)), dim3(block), params, 0, s);
 }
 
+template <int BLOCK>
+constexpr int q_slots() { return BLOCK == Q_BLOCK_CHUNK ? Q_SLOTS_CHUNK : Q_SLOTS_LAYER; }
+
+template <typename TIn, int BLOCK, bool MUL>
+constexpr auto coop_quantize_kernel() {
+    if constexpr (BLOCK == Q_BLOCK_CHUNK) return k_quantize_chunk<TIn, q_slots<BLOCK>(), BLOCK, MUL>;
+    else return k_quantize_layer<TIn, q_slots<BLOCK>(), BLOCK, MUL>;
+}
+
+template <typename TIn, int BLOCK, bool MUL>
+hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
+    const dim3 block(BLOCK);
+    const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
+    if (a.amax != nullptr) {
+        hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
+    const int64_t resident = resident_groups<coop>(BLOCK);
+    if (resident >= t.big_max_count) {
+        // small units: one wave each; the others: the persistent kernel
+        if (t.n_small > 0) {
+            const int64_t items = static_cast<int64_t>(a.W) * t.n_small;
+            const unsigned nb = static_cast<unsigned>((items + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
+            hipLaunchKernelGGL((k_quantize_small<TIn, SMALL_SLOTS_Q, MUL>), dim3(nb), dim3(SMALL_BLOCK),
+                               0, s, a);
+        }
+        if (t.n_big > 0) {
+            QArgs c = a;
+            c.tiles = t.d_big;
+            c.n_tiles = t.n_big;
+            const int64_t work = static_cast<int64_t>(a.W) * t.n_big;
+            hipError_t e = launch_coop(coop, work < resident ? work : resident, BLOCK, c, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipGetLastError();
+    }
+    // a unit with more tiles than resident work groups: two launches
+    QArgs p = a;
+    p.list = t.d_multi;
+    hipLaunchKernelGGL((k_tile_absmax<TIn, q_slots<BLOCK>(), BLOCK>),
+                       dim3(static_cast<unsigned>(t.n_multi), static_cast<unsigned>(a.W)), block, 0, s, p);
+    hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_FUSED>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <typename TIn, bool MUL>
 hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
     QArgs a = a0;
@@ -942,25 +1152,16 @@ hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
     a.cnt = t.d_cnt;
     a.ctl = t.d_ctl;
     a.n_multi_units = t.n_multi_units;
-    const dim3 block(Q_BLOCK);
+    a.small = t.d_small;
+    a.n_small = t.n_small;
+    if (t.block == Q_BLOCK_CHUNK) return quantize_geom<TIn, Q_BLOCK_CHUNK, MUL>(a, t, s);
+    return quantize_geom<TIn, Q_BLOCK_LAYER, MUL>(a, t, s);
+}
+
+template <typename TIn, int BLOCK>
+void absmax_geom(const QArgs &a, const Table &t, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
-    if (a.amax != nullptr) {
-        hipLaunchKernelGGL((k_quantize<TIn, Q_SLOTS, Q_BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
-        return hipGetLastError();
-    }
-    constexpr auto coop = k_quantize_coop<TIn, Q_SLOTS, Q_BLOCK, MUL>;
-    const int64_t resident = resident_groups<coop>(Q_BLOCK);
-    if (resident >= t.max_count) {
-        const int64_t work = static_cast<int64_t>(a.W) * t.n_tiles;
-        return launch_coop(coop, work < resident ? work : resident, Q_BLOCK, a, s);
-    }
-    // a unit with more tiles than resident work groups: two launches
-    QArgs p = a;
-    p.list = t.d_multi;
-    hipLaunchKernelGGL((k_tile_absmax<TIn, Q_SLOTS, Q_BLOCK>),
-                       dim3(static_cast<unsigned>(t.n_multi), static_cast<unsigned>(a.W)), block, 0, s, p);
-    hipLaunchKernelGGL((k_quantize<TIn, Q_SLOTS, Q_BLOCK, MUL, Q_FUSED>), grid, block, 0, s, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL((k_tile_absmax<TIn, q_slots<BLOCK>(), BLOCK>), grid, dim3(BLOCK), 0, s, a);
 }
 
 }  // namespace
@@ -968,26 +1169,30 @@ hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
 // ---- launchers ----------------------------------------------------------------------------
 
 hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream_t s) {
+    if (!table_ready(t, a0.n_units)) return hipErrorInvalidValue;
     QArgs a = a0;
     a.list = nullptr;
     a.partial = t.d_partial;
     a.unit_first = t.d_unit_first;
     a.tiles = t.d_tiles;
     const bool mul = a.in_mul != 1.0f;
-    const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
     const int64_t total = static_cast<int64_t>(a.W) * a.n_units;
     const unsigned nb = static_cast<unsigned>((total + 255) / 256);
+    const bool chunk = t.block == Q_BLOCK_CHUNK;
     if (dt == GQ_F32) {
-        hipLaunchKernelGGL((k_tile_absmax<float, Q_SLOTS, Q_BLOCK>), grid, dim3(Q_BLOCK), 0, s, a);
+        if (chunk) absmax_geom<float, Q_BLOCK_CHUNK>(a, t, s);
+        else absmax_geom<float, Q_BLOCK_LAYER>(a, t, s);
         hipLaunchKernelGGL(k_absmax_finalize<float>, dim3(nb), dim3(256), 0, s, a, mul);
     } else {
-        hipLaunchKernelGGL((k_tile_absmax<__half, Q_SLOTS, Q_BLOCK>), grid, dim3(Q_BLOCK), 0, s, a);
+        if (chunk) absmax_geom<__half, Q_BLOCK_CHUNK>(a, t, s);
+        else absmax_geom<__half, Q_BLOCK_LAYER>(a, t, s);
         hipLaunchKernelGGL(k_absmax_finalize<__half>, dim3(nb), dim3(256), 0, s, a, mul);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s) {
+    if (!table_ready(t, a.n_units)) return hipErrorInvalidValue;
     const bool mul = a.in_mul != 1.0f;
     if (dt == GQ_F32)
         return mul ? quantize_typed<float, true>(a, t, s) : quantize_typed<float, false>(a, t, s);
@@ -995,6 +1200,7 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
 }
 
 hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipStream_t s) {
+    if (!table_ready(t, 1)) return hipErrorInvalidValue;
     RArgs a = a0;
     a.tiles = t.d_tiles;
     a.partial = t.d_partial;
@@ -1012,8 +1218,23 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipSt
     }
     constexpr auto coop = k_reduce_coop<R_SLOTS, R_BLOCK>;
     const int64_t resident = resident_groups<coop>(R_BLOCK);
-    if (resident >= t.max_count) {
-        return launch_coop(coop, t.n_tiles < resident ? t.n_tiles : resident, R_BLOCK, a, s);
+    if (resident >= t.big_max_count) {
+        if (t.n_small > 0) {
+            RArgs c = a;
+            c.small = t.d_small;
+            c.n_small = t.n_small;
+            const unsigned nb =
+                static_cast<unsigned>((t.n_small + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
+            hipLaunchKernelGGL((k_reduce_small<SMALL_SLOTS_R>), dim3(nb), dim3(SMALL_BLOCK), 0, s, c);
+        }
+        if (t.n_big > 0) {
+            RArgs c = a;
+            c.tiles = t.d_big;
+            c.n_tiles = t.n_big;
+            hipError_t e = launch_coop(coop, t.n_big < resident ? t.n_big : resident, R_BLOCK, c, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipGetLastError();
     }
     RArgs p = a;
     p.list = t.d_multi;

@@ -16,11 +16,13 @@ SO = os.path.join(HERE, "_lib", "libgq.so")
 
 GQ_OK, GQ_ERR_INVALID, GQ_ERR_ALIGN, GQ_ERR_CAPACITY, GQ_ERR_HIP, GQ_ERR_DEVICE = range(6)
 GQ_F32, GQ_F16 = 0, 1
+GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
 GQ_MAX_RANKS = 64
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
-           "gq_units_destroy", "gq_units_info", "gq_units_faults", "gq_absmax", "gq_quantize",
+           "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_faults",
+           "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize")
 
 
@@ -49,6 +51,8 @@ def _load():
     L.gq_units_destroy.argtypes = [vp]
     L.gq_units_info.restype = st
     L.gq_units_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.gq_units_schedule.restype = st
+    L.gq_units_schedule.argtypes = [vp, i32, ctypes.POINTER(i32)]
     L.gq_units_faults.restype = st
     L.gq_units_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
     L.gq_absmax.restype = st
@@ -157,6 +161,14 @@ def gq_units_info(units):
     n, u = ctypes.c_int64(0), ctypes.c_int64(0)
     _check(lib.gq_units_info(units.handle, ctypes.byref(n), ctypes.byref(u)))
     return n.value, u.value
+
+
+def gq_units_schedule(units, dtype_code=GQ_F32):
+    """GQ_SCHED_LAYER or GQ_SCHED_CHUNK: the fused quantize schedule chosen
+    for this table and element type."""
+    v = ctypes.c_int32(-1)
+    _check(lib.gq_units_schedule(units.handle, dtype_code, ctypes.byref(v)))
+    return v.value
 
 
 def gq_units_faults(units):

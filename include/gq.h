@@ -124,6 +124,17 @@ gq_status gq_units_destroy(gq_units *u);
 gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
 
 /*
+ * gq_units_schedule -- which schedule the fused quantize of a table uses for
+ * elements of type dt: GQ_SCHED_LAYER (units spanning many work-group
+ * tiles: per-tensor or per-layer scales) or GQ_SCHED_CHUNK (most elements
+ * in units of at most one 128 KiB tile: per-chunk scales, small tensors).
+ * Chosen when the table is created; results do not depend on it.
+ */
+#define GQ_SCHED_LAYER 0
+#define GQ_SCHED_CHUNK 1
+gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
+
+/*
  * gq_units_faults -- number of bounded waits that gave up since the table
  * was created (0 unless the device failed to keep the cooperative work
  * groups of a launch resident; the results of such a launch are invalid).

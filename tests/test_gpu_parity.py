@@ -200,6 +200,31 @@ def test_unit_larger_than_resident_groups(gq, oracle, kind):
                      modes=("fused",))
 
 
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+def test_both_quantize_schedules(gq, oracle, kind):
+    """The same data under a per-chunk unit table (chunk schedule) and a
+    per-tensor table (layer schedule): both match the oracle."""
+    rng = np.random.default_rng(31 + kind)
+    esz = 4 if kind == F32 else 2
+    sizes = [2_000_003, 600_000, 1_000, 1_200_000]
+    chunk_off = [np.zeros(1, np.int64)]
+    base = 0
+    for sz in sizes:
+        chunk_off.append(gq.gq_plan_chunks(sz, esz)[1:] + base)
+        base += sz
+    chunk_off = np.concatenate(chunk_off)
+    tensor_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(tensor_off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(3)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    u1 = gq.gq_units_create(chunk_off)
+    u2 = gq.gq_units_create(tensor_off)
+    assert gq.gq_units_schedule(u1, kind) == gq.GQ_SCHED_CHUNK
+    assert gq.gq_units_schedule(u2, kind) == gq.GQ_SCHED_LAYER
+    _run_and_compare(gq, oracle, xs, kind, chunk_off, in_mul, "chunk_sched_k%d" % kind)
+    _run_and_compare(gq, oracle, xs, kind, tensor_off, in_mul, "layer_sched_k%d" % kind)
+
+
 def test_errors_on_device(gq):
     """Argument errors reported by the ABI leave outputs untouched."""
     import torch
