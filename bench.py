@@ -16,6 +16,7 @@ Prints one JSON line.  The default workload is the ResNet-152 gradient set
 buckets); --workload picks another of the five synthetic workloads.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
 METRIC = "GB/s gradient input quantized+reduced on 1 MI355X; % of HBM peak"
+KERNEL_SRC = os.path.join(ROOT, "gradient_compression_allreduce_amd", "csrc", "gq_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(PROFILES, "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def log(*a):
@@ -165,6 +191,13 @@ def main():
     value = input_bytes / (ms * 1e-3) / 1e9
     b_alg = bq + br
     q_achieved = bq / (q_ms * 1e-3) / 1e9
+    faults = gq.gq_units_faults(units)
+    if faults:
+        print("a bounded cross-group wait gave up %d times: results invalid" % faults,
+              file=sys.stderr)
+        sys.exit(3)
+    sched = gq.gq_units_schedule(units, gq.GQ_F32 if kind == 0 else gq.GQ_F16)
+    qkernel = "k_quantize_chunk" if sched == gq.GQ_SCHED_CHUNK else "k_quantize_layer"
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -186,11 +219,14 @@ def main():
         "hbm_fraction": round(b_alg / (ms * 1e-3) / HBM_PEAK, 4),
         "algorithmic_bytes_per_step": b_alg,
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gq_quantize (all ranks)",
+        # the quantize stage is one launch of the persistent quantize kernel
+        "roofline": {"bound": "hbm", "kernel": qkernel,
                      "achieved": round(q_achieved, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(q_achieved / (HBM_PEAK / 1e9), 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(qkernel, w.name),
+                     "algorithmic_bytes_per_launch": bq},
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "kernel_source": kernel_source_hash(),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -48,11 +48,10 @@ constexpr int R_BLOCK = 512;
 constexpr int R_SLOTS = 1;           // 16 codes = 16 sums per thread (8192 per tile)
 
 // Units whose 16-byte slots span at most 64 * SMALL_SLOTS[table] slots are
-// "small": one wave handles a whole unit in a plain (non-persistent) launch,
-// with no tile exchange and no ticket.
-constexpr int SMALL_BLOCK = 256;     // four waves, four units per work group
+// "small": one wave handles a whole unit, in a first phase of the
+// persistent kernel, with no tile exchange and no ticket.
 constexpr int SMALL_SLOTS_Q = 16;    // fp32: 4096 elements, fp16: 8192 elements
-constexpr int SMALL_SLOTS_R = 4;     // 4096 elements
+constexpr int SMALL_SLOTS_R = 2;     // 2048 elements
 
 constexpr int kSlotElems[TAB_COUNT] = {4, 8, 16};  // V of each table
 

@@ -9,21 +9,24 @@
 // 1 KiB of contiguous memory per load instruction, and the tile stays in
 // registers between the max and the code pass.
 //
-// The hot path is one persistent, cooperatively launched kernel per stage.
-// Work groups take tiles in order from a ticket counter (tickets run over
-// ranks, then tiles in unit order), so the tiles of one unit start at about
-// the same time.  A unit larger than one tile combines its tiles' maxima in
-// device memory (see "cross-work-group max" below) and each of its tiles
-// waits, bounded, for the others, so every input byte is read from HBM
-// once.  A work group blocks only in that wait, and by then it has
-// published every tile it holds of that unit (it may hold the next tile,
-// loaded or summed ahead to overlap memory latency).  So if all work groups
-// were blocked, the earliest unit any of them waits on would have all of
-// its taken tiles published and at least one tile untaken, which needs
-// every one of the G resident work groups to hold one of its tiles: a unit
-// of more than G tiles.  Resident groups are guaranteed by the cooperative
-// launch, and units of more than G tiles take a two-launch fallback (per-tile
-// maxima, then a re-reading quantize pass).
+// The hot path is one persistent kernel per stage, launched with no more
+// work groups (G) than the device keeps resident at once.  Work groups take
+// tiles in order from a ticket counter (tickets run over ranks, then tiles
+// in unit order), so the tiles of one unit start at about the same time.  A
+// unit larger than one tile combines its tiles' maxima in device memory
+// (see "cross-work-group max" below) and each of its tiles waits, bounded,
+// for the others, so every input byte is read from HBM once.  A work group
+// blocks only in that wait, and by then it has published every tile it
+// holds.  So if all running work groups were blocked, the earliest unit any
+// of them waits on would have all of its taken tiles published and at least
+// one tile untaken, which needs every running work group to hold one of its
+// tiles.  A work group takes tickets only once it runs, and the grid alone
+// fits on the device, so every work group eventually runs (as soon as any
+// other work on the device has finished) and the wait ends for units of up
+// to G tiles.  Larger units take a two-launch fallback (per-tile maxima,
+// then a re-reading quantize pass).  Every wait is bounded: if one ever
+// gives up (the device did not run the grid), a fault counter records it
+// and the launch's results are invalid.
 //
 // Numerics (must match the CPU oracle bit for bit):
 //   * g = x * in_mul is one rounded binary32 multiply (skipped when
@@ -540,6 +543,32 @@ __device__ __forceinline__ Tile load_desc(const Tile *tiles, int64_t i) {
 
 // ---- quantize kernels -------------------------------------------------------------
 
+// Small units: one wave per (rank, unit), no tile exchange and no ticket.
+// `item` runs over ranks, then small units.
+template <typename TIn, int SS, bool MUL>
+__device__ __forceinline__ void quantize_small_unit(const QArgs &a, int64_t item) {
+    using Raw = typename In<TIn>::Raw;
+    const int w = static_cast<int>(item / a.n_small);
+    const Tile t = load_desc(a.small, item - static_cast<int64_t>(w) * a.n_small);
+    Raw raw[SS];
+    const uint32_t m = wave_max(load_tile<TIn, SS, 64>(a.x[w], t, a.n, raw));
+    const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
+    if ((threadIdx.x & 63) == 0) a.scale[w][t.unit] = sc;
+    quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
+}
+
+// First phase of the persistent kernels: wave v of work group g takes the
+// small items v + waves * (g + G * k).  Ends with a work-group barrier.
+template <int BLOCK, typename F>
+__device__ __forceinline__ void small_phase(int64_t items, F &&one) {
+    constexpr int WPG = BLOCK / 64;
+    const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t item = static_cast<int64_t>(blockIdx.x) * WPG + wave; item < items;
+         item += static_cast<int64_t>(gridDim.x) * WPG)
+        one(item);
+    __syncthreads();
+}
+
 // Hot path, SCHED_CHUNK: every tile of every rank, one read of the input.
 // Per tile, a work group: issues the loads of its next tile; writes the codes of its
 // current tile (whose unit max it already has), so the loads are in flight
@@ -550,6 +579,9 @@ template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_chunk(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
+    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
+        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+    });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, ticket
     const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
@@ -627,6 +659,9 @@ template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_layer(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
+    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
+        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+    });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
     const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
@@ -692,23 +727,6 @@ void k_quantize_layer(const QArgs a) {
         arr_c = arr_n;
     }
     launch_exit(a.ctl);
-}
-
-// Small units: one wave per (rank, unit), four per work group, no tile
-// exchange and no ticket.
-template <typename TIn, int SS, bool MUL>
-__global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
-    using Raw = typename In<TIn>::Raw;
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= static_cast<int64_t>(a.W) * a.n_small) return;
-    const int w = static_cast<int>(item / a.n_small);
-    const Tile t = a.small[item - static_cast<int64_t>(w) * a.n_small];
-    Raw raw[SS];
-    const uint32_t m = wave_max(load_tile<TIn, SS, 64>(a.x[w], t, a.n, raw));
-    const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
-    if ((threadIdx.x & 63) == 0) a.scale[w][t.unit] = sc;
-    quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
 }
 
 // Fallback pass 1 (and gq_absmax): per-tile max of the listed tiles.
@@ -930,6 +948,19 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
     else requantize_tile_mode<S, BLOCK, CM_ZERO>(t, acc, p, q);
 }
 
+// Small units: one wave per unit.
+template <int SR>
+__device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item) {
+    const Tile t = load_desc(a.small, item);
+    float acc[SR][RV];
+    reduce_tile<SR, 64, 1>(a, t, acc);
+    if (a.r) store_sum<SR, 64>(t, acc, a.r);
+    const uint32_t m = wave_max(acc_absmax<SR>(acc));
+    const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+    if ((threadIdx.x & 63) == 0) a.scale_out[t.unit] = sc;
+    requantize_tile<SR, 64>(t, acc, quant_params(sc, true), a.q_out);
+}
+
 // Hot path: reduce + requantize of every tile, one read of the codes.  A
 // work group sums its next tile (and publishes that tile's max) before it
 // waits for the current tile's unit max, so the wait overlaps a whole tile
@@ -937,6 +968,7 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
 template <int S, int BLOCK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_reduce_coop(const RArgs a) {
+    small_phase<BLOCK>(a.n_small, [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R>(a, item); });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
     const int64_t total = a.n_tiles;
@@ -1001,22 +1033,6 @@ void k_reduce_coop(const RArgs a) {
         tk = tn;
     }
     launch_exit(a.ctl);
-}
-
-// Small units: one wave per unit, four per work group.
-template <int SR>
-__global__ __launch_bounds__(SMALL_BLOCK) void k_reduce_small(const RArgs a) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.n_small) return;
-    const Tile t = a.small[item];
-    float acc[SR][RV];
-    reduce_tile<SR, 64, 1>(a, t, acc);
-    if (a.r) store_sum<SR, 64>(t, acc, a.r);
-    const uint32_t m = wave_max(acc_absmax<SR>(acc));
-    const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
-    if ((threadIdx.x & 63) == 0) a.scale_out[t.unit] = sc;
-    requantize_tile<SR, 64>(t, acc, quant_params(sc, true), a.q_out);
 }
 
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
@@ -1088,12 +1104,14 @@ int64_t resident_groups(int block) {
     return cached;
 }
 
+// A persistent kernel: `groups` never exceeds the resident capacity.  (A
+// cooperative launch would also guarantee co-residency, but with the ROCm
+// runtime it costs about 20 us of extra queue synchronization per launch,
+// and the schedule above needs only that the grid fits.)
 template <typename K, typename A>
-hipError_t launch_coop(K kernel, int64_t groups, int block, const A &args, hipStream_t s) {
-    A copy = args;
-    void *params[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                      dim3(static_cast<unsigned>(groups)), dim3(block), params, 0, s);
+hipError_t launch_persistent(K kernel, int64_t groups, int block, const A &args, hipStream_t s) {
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(groups)), dim3(block), 0, s, args);
+    return hipGetLastError();
 }
 
 template <int BLOCK>
@@ -1116,22 +1134,16 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
     constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
     const int64_t resident = resident_groups<coop>(BLOCK);
     if (resident >= t.big_max_count) {
-        // small units: one wave each; the others: the persistent kernel
-        if (t.n_small > 0) {
-            const int64_t items = static_cast<int64_t>(a.W) * t.n_small;
-            const unsigned nb = static_cast<unsigned>((items + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
-            hipLaunchKernelGGL((k_quantize_small<TIn, SMALL_SLOTS_Q, MUL>), dim3(nb), dim3(SMALL_BLOCK),
-                               0, s, a);
-        }
-        if (t.n_big > 0) {
-            QArgs c = a;
-            c.tiles = t.d_big;
-            c.n_tiles = t.n_big;
-            const int64_t work = static_cast<int64_t>(a.W) * t.n_big;
-            hipError_t e = launch_coop(coop, work < resident ? work : resident, BLOCK, c, s);
-            if (e != hipSuccess) return e;
-        }
-        return hipGetLastError();
+        // one launch: small units first (one wave each), then the tiles of
+        // the others through the ticket counter
+        QArgs c = a;
+        c.tiles = t.d_big;
+        c.n_tiles = t.n_big;
+        const int64_t small_groups =
+            (static_cast<int64_t>(a.W) * t.n_small + BLOCK / 64 - 1) / (BLOCK / 64);
+        int64_t groups = static_cast<int64_t>(a.W) * t.n_big;
+        if (small_groups > groups) groups = small_groups;
+        return launch_persistent(coop, groups < resident ? groups : resident, BLOCK, c, s);
     }
     // a unit with more tiles than resident work groups: two launches
     QArgs p = a;
@@ -1219,22 +1231,14 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipSt
     constexpr auto coop = k_reduce_coop<R_SLOTS, R_BLOCK>;
     const int64_t resident = resident_groups<coop>(R_BLOCK);
     if (resident >= t.big_max_count) {
-        if (t.n_small > 0) {
-            RArgs c = a;
-            c.small = t.d_small;
-            c.n_small = t.n_small;
-            const unsigned nb =
-                static_cast<unsigned>((t.n_small + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
-            hipLaunchKernelGGL((k_reduce_small<SMALL_SLOTS_R>), dim3(nb), dim3(SMALL_BLOCK), 0, s, c);
-        }
-        if (t.n_big > 0) {
-            RArgs c = a;
-            c.tiles = t.d_big;
-            c.n_tiles = t.n_big;
-            hipError_t e = launch_coop(coop, t.n_big < resident ? t.n_big : resident, R_BLOCK, c, s);
-            if (e != hipSuccess) return e;
-        }
-        return hipGetLastError();
+        RArgs c = a;
+        c.small = t.d_small;
+        c.n_small = t.n_small;
+        c.tiles = t.d_big;
+        c.n_tiles = t.n_big;
+        const int64_t small_groups = (t.n_small + R_BLOCK / 64 - 1) / (R_BLOCK / 64);
+        const int64_t groups = t.n_big > small_groups ? t.n_big : small_groups;
+        return launch_persistent(coop, groups < resident ? groups : resident, R_BLOCK, c, s);
     }
     RArgs p = a;
     p.list = t.d_multi;

@@ -136,8 +136,10 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 
 /*
  * gq_units_faults -- number of bounded waits that gave up since the table
- * was created (0 unless the device failed to keep the cooperative work
- * groups of a launch resident; the results of such a launch are invalid).
+ * was created.  The persistent kernels size their grid to what the device
+ * keeps resident; a wait can only give up (after about a second) if the
+ * device did not run the whole grid, e.g. while other long-running work
+ * held its compute units.  The results of such a launch are invalid.
  * Synchronizes the device.  count: host pointer receiving the number.
  */
 gq_status gq_units_faults(const gq_units *u, uint64_t *count);
