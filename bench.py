@@ -78,18 +78,43 @@ def algorithmic_bytes(W, n, e, U):
     return bq, br
 
 
-def cpu_baseline(w, xs, off, kind):
-    """The oracle as it stands (single-threaded C), on the same host inputs."""
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, xs, off, kind, min_seconds=10.0, max_reps=20):
+    """The oracle as it stands (single-threaded C), on the same host inputs,
+    pinned to one host core; the whole workload is repeated until about
+    `min_seconds` of CPU work have been timed."""
     from oracle import Oracle
     o = Oracle()
-    t0 = time.perf_counter()
-    o.allreduce_step(xs, kind, off, w.in_mul)
-    dt = time.perf_counter() - t0
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        times = []
+        while True:
+            t0 = time.perf_counter()
+            o.allreduce_step(xs, kind, off, w.in_mul)
+            times.append(time.perf_counter() - t0)
+            if sum(times) >= min_seconds or len(times) >= max_reps:
+                break
+    finally:
+        os.sched_setaffinity(0, old_aff)
+    dt = float(np.median(times))
     nbytes = w.W * w.n * w.elem_bytes
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": dt,
-            "sample": "the whole workload (%d ranks x %d elements): quantize, rank-order "
-                      "reduce and requantize, one host thread" % (w.W, w.n)}
+            "seconds_per_step": dt, "repetitions": len(times),
+            "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
+            "sample": "the whole workload (%d ranks x %d elements), repeated %d times "
+                      "(median): quantize, rank-order reduce and requantize, one host "
+                      "thread pinned to core %d" % (w.W, w.n, len(times), core)}
 
 
 def main():
@@ -100,6 +125,10 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-reps", type=int, default=None,
+                    help="also time the step replayed from a HIP graph of this many "
+                         "repetitions (default: 100 for the launch-bound 1M-element "
+                         "workload, else off)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the simulated ranks all live in one device's "
@@ -115,6 +144,8 @@ def main():
     from gradient_compression_allreduce_amd import gq
 
     w = get_workload(args.workload, seed=args.seed)
+    if args.graph_reps is None:
+        args.graph_reps = 100 if args.workload == 1 else 0
     kind = 0 if w.kind == "f32" else 1
     off = unit_offsets(w, gq.gq_plan_chunks)
     U = off.size - 1
@@ -171,6 +202,32 @@ def main():
     ms = total_ms / args.steps
     q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     r_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+
+    graph = None
+    if args.graph_reps > 0:
+        # the same step, captured once into a HIP graph of graph_reps
+        # repetitions (launch-bound workloads); no allocation or memset is
+        # recorded: the library's compute calls make none
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(args.graph_reps):
+                    gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=cap)
+                    gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"reps": args.graph_reps,
+                 "ms_per_step": round(g0.elapsed_time(g1) / args.graph_reps, 4)}
+        del g
 
     # practical ceiling: a plain device-to-device copy of the same volume
     bq, br = algorithmic_bytes(w.W, w.n, w.elem_bytes, U)
@@ -218,7 +275,10 @@ def main():
                    "seed": args.seed},
         "hbm_fraction": round(b_alg / (ms * 1e-3) / HBM_PEAK, 4),
         "algorithmic_bytes_per_step": b_alg,
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
+        "graph": graph,
         # the quantize stage is one launch of the persistent quantize kernel
         "roofline": {"bound": "hbm", "kernel": qkernel,
                      "achieved": round(q_achieved, 1), "peak": HBM_PEAK / 1e9,
@@ -233,7 +293,7 @@ def main():
         log("timing the CPU oracle on the same inputs ...")
         rec["cpu_baseline"] = cpu_baseline(w, xs, off, kind)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 4)
-        rec["cpu_baseline"]["seconds"] = round(rec["cpu_baseline"]["seconds"], 2)
+        rec["cpu_baseline"]["seconds_per_step"] = round(rec["cpu_baseline"]["seconds_per_step"], 3)
     print(json.dumps(rec), flush=True)
 
 

@@ -243,3 +243,52 @@ def test_errors_on_device(gq):
     assert float(s[0]) == 7.0 and int(q[0]) == 5
     n, U = gq.gq_units_info(units)
     assert (n, U) == (100, 1)
+
+
+def test_graph_replays_match_eager(gq, oracle):
+    """The step captured once into a HIP graph and replayed on new inputs,
+    with eager library calls and other device work between replays: every
+    replay matches the oracle (the persistent kernels' device-side launch
+    state carries over between graph and eager launches)."""
+    import torch
+    rng = np.random.default_rng(41)
+    n = 300_001
+    off = _offsets(rng, n, 1, 120_000)
+    n = int(off[-1])
+    W = 4
+    step = GpuStep(gq, off, W, F32, n)
+    dx = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(W)]
+    for d in dx:
+        d.zero_()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            gq.gq_quantize(dx, step.units, step.scales, step.codes, stream=cap)
+            gq.gq_reduce_requantize(step.codes, step.scales, step.units, step.scale_out,
+                                    step.q_out, r_out=step.r, stream=cap)
+    torch.cuda.synchronize()
+    other = GpuStep(gq, off, W, F32, n)
+    for rep in range(3):
+        xs = [_grad(rng, n, F32) for _ in range(W)]
+        for d, x in zip(dx, xs):
+            d.copy_(torch.from_numpy(x))
+        say("graph replay", rep)
+        g.replay()
+        got = step.host()
+        compare_step(got, oracle.allreduce_step(xs, F32, off), W, label="graph%d" % rep)
+        # eager work between replays: the same kernels on the same unit
+        # table (whose device-side launch state the graph's kernels share),
+        # into other outputs
+        step_xs = [_grad(rng, n, F32) for _ in range(W)]
+        ex = [to_device(x) for x in step_xs]
+        gq.gq_quantize(ex, step.units, other.scales, other.codes)
+        gq.gq_reduce_requantize(other.codes, other.scales, step.units, other.scale_out,
+                                other.q_out, r_out=other.r)
+        torch.cuda.synchronize()
+        assert gq.gq_units_faults(step.units) == 0
+        compare_step(other.host(), oracle.allreduce_step(step_xs, F32, off), W,
+                     label="eager%d" % rep)
+    del g
