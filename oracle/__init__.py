@@ -8,7 +8,8 @@ A thin ctypes wrapper over liboracle.so (oracle.c, plain single-threaded C,
 built with -O2 -ffp-contract=off).  Each function follows one step of the
 pipelined HCCL AllReduce article (bjdmk.com.cn/news/6235379): §2.1 chunk
 plan, §2.2.1 absmax scale / int8 codes / INT8 AllReduce reduction, §6.1
-unscale on load.
+unscale on load, and §5.2's check with quantization switched off (the fp32
+reference sum and the per-unit error report).
 """
 import ctypes
 import os
@@ -22,6 +23,8 @@ SRC = os.path.join(HERE, "oracle.c")
 SO = os.path.join(HERE, "liboracle.so")
 
 F32, F16 = 0, 1
+STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
+         "mean_rel_err", "sum_dd", "sum_rr", "sum_dr", "cos")
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
           "-shared", "-Wall", "-Wextra"]
 
@@ -61,6 +64,10 @@ def _declare(L):
     L.oracle_reduce_dequant.argtypes = [vp, vp, i32, i64, vp, i64, vp]
     L.oracle_requantize.restype = None
     L.oracle_requantize.argtypes = [vp, i64, vp, i64, vp, vp]
+    L.oracle_sum_f32.restype = None
+    L.oracle_sum_f32.argtypes = [vp, i32, f32, i32, i64, i32, vp]
+    L.oracle_error_report.restype = None
+    L.oracle_error_report.argtypes = [vp, vp, vp, i64, vp, i64, vp]
     return L
 
 
@@ -178,3 +185,29 @@ class Oracle:
         s2, q2 = self.requantize(r, off)
         return {"amax": [p[0] for p in per], "scale": ss, "q": qs, "r": r,
                 "scale_out": s2, "q_out": q2}
+
+    def sum_f32(self, xs, kind, in_mul=1.0, mean=False):
+        """fp32 rank-order sum of the loaded gradients (÷W if mean)."""
+        xs = [np.ascontiguousarray(x) for x in xs]
+        W = len(xs)
+        n = xs[0].size
+        assert all(x.size == n for x in xs)
+        xp = (ctypes.c_void_p * W)(*[x.ctypes.data for x in xs])
+        r = np.empty(n, dtype=np.float32)
+        self.L.oracle_sum_f32(ctypes.cast(xp, ctypes.c_void_p), kind, in_mul, W, n,
+                              1 if mean else 0, r.ctypes.data)
+        return r
+
+    def error_report(self, q, scale, ref, off):
+        """-> float64 array [U, 10], columns named by STATS."""
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        ref = np.ascontiguousarray(ref, dtype=np.float32)
+        off = np.ascontiguousarray(off, dtype=np.int64)
+        U = off.size - 1
+        n = int(off[-1])
+        assert q.size >= n and ref.size >= n and scale.size >= U
+        out = np.empty((U, len(STATS)), dtype=np.float64)
+        self.L.oracle_error_report(q.ctypes.data, scale.ctypes.data, ref.ctypes.data, n,
+                                   off.ctypes.data, U, out.ctypes.data)
+        return out

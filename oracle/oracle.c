@@ -222,3 +222,92 @@ void oracle_requantize(const float *r, int64_t n, const int64_t *off,
     oracle_quantize_units(r, ORACLE_F32, 1.0f, n, off, n_units, NULL,
                           scale_out, q_out);
 }
+
+/* fp32 reference for the A/B check: the same rank-order reduction as the
+ * INT8 path, on the unquantized gradients. */
+void oracle_sum_f32(const void *const *x, int32_t kind, float in_mul, int32_t W,
+                    int64_t n, int32_t mean, float *r_out)
+{
+    float *g = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (g == NULL)
+        abort();
+    for (int64_t i = 0; i < n; ++i)
+        r_out[i] = 0.0f;
+    for (int32_t rank = 0; rank < W; ++rank) {
+        oracle_load(x[rank], kind, in_mul, n, g);
+        for (int64_t i = 0; i < n; ++i)
+            r_out[i] = r_out[i] + g[i];
+    }
+    if (mean)
+        for (int64_t i = 0; i < n; ++i)
+            r_out[i] = r_out[i] / (float)W;
+    free(g);
+}
+
+static uint64_t d2u(double d)
+{
+    union { double d; uint64_t u; } c;
+    c.d = d;
+    return c.u;
+}
+
+static double u2d(uint64_t u)
+{
+    union { double d; uint64_t u; } c;
+    c.u = u;
+    return c.d;
+}
+
+/* |a| as a bit pattern, ordered like the value, NaN above +inf. */
+static uint64_t abs_bits(double a)
+{
+    return d2u(a) & 0x7fffffffffffffffull;
+}
+
+static double ratio_or_zero(double a, double b)
+{
+    if (a == 0.0 && b == 0.0)
+        return 0.0;
+    return a / b;
+}
+
+void oracle_error_report(const int8_t *q, const float *scale, const float *ref,
+                         int64_t n, const int64_t *off, int64_t n_units,
+                         double *stats_out)
+{
+    (void)n;
+    for (int64_t u = 0; u < n_units; ++u) {
+        uint64_t max_err = 0, max_ref = 0;
+        double sum_err = 0.0, sum_ref = 0.0, dd = 0.0, rr = 0.0, dr = 0.0;
+        for (int64_t i = off[u]; i < off[u + 1]; ++i) {
+            double d = (double)((float)q[i] * scale[u]);
+            double r = (double)ref[i];
+            double e = fabs(d - r);
+            if (abs_bits(e) > max_err)
+                max_err = abs_bits(e);
+            if (abs_bits(r) > max_ref)
+                max_ref = abs_bits(r);
+            sum_err = sum_err + e;
+            sum_ref = sum_ref + fabs(r);
+            dd = dd + d * d;
+            rr = rr + r * r;
+            dr = dr + d * r;
+        }
+        double *o = stats_out + ORACLE_STATS * u;
+        o[0] = u2d(max_err);
+        o[1] = u2d(max_ref);
+        o[2] = ratio_or_zero(o[0], o[1]);
+        o[3] = sum_err;
+        o[4] = sum_ref;
+        o[5] = ratio_or_zero(sum_err, sum_ref);
+        o[6] = dd;
+        o[7] = rr;
+        o[8] = dr;
+        if (dd == 0.0 && rr == 0.0)
+            o[9] = 1.0;
+        else if (dd == 0.0 || rr == 0.0)
+            o[9] = 0.0;
+        else
+            o[9] = dr / sqrt(dd * rr);
+    }
+}

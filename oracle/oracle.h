@@ -84,6 +84,43 @@ void oracle_reduce_dequant(const int8_t *const *q, const float *const *s,
 void oracle_requantize(const float *r, int64_t n, const int64_t *off,
                        int64_t n_units, float *scale_out, int8_t *q_out);
 
+/* ---- Unquantized A/B path and error report ------------------------------
+ * The article's troubleshooting section (gradient anomalies) checks whether
+ * a problem comes from precision by switching gradient quantization off;
+ * the torchtitan-npu article's mixed-precision listing all-reduces fp32
+ * gradients and divides them by the data-parallel group size.  These two
+ * functions give that fp32 reference next to the INT8 path and measure the
+ * INT8 result against it. */
+
+/* fp32 AllReduce reduction on one device, no quantization:
+ *   r = (((+0 + g_0) + g_1) + ...) + g_{W-1},  g_w = load(x_w) as above,
+ * each sum rounded to binary32, ranks in order; with mean != 0 the sum is
+ * then divided by W (one binary32 division). */
+void oracle_sum_f32(const void *const *x, int32_t kind, float in_mul, int32_t W,
+                    int64_t n, int32_t mean, float *r_out);
+
+/* Per-unit error statistics of an INT8 result against a reference, all in
+ * binary64.  d_i = float(q_i) * s_u (binary32, one rounding) is the value
+ * the codes stand for; ref_i is the reference.  Field order of the 10
+ * doubles written per unit to stats_out[10*u ...]:
+ *   0 max_abs_err   max_i |d_i - ref_i|     (difference in binary64)
+ *   1 max_abs_ref   max_i |ref_i|
+ *   2 max_rel_err   max_abs_err / max_abs_ref
+ *   3 sum_abs_err   sum_i |d_i - ref_i|     (element order)
+ *   4 sum_abs_ref   sum_i |ref_i|
+ *   5 mean_rel_err  sum_abs_err / sum_abs_ref
+ *   6 sum_dd        sum_i d_i^2
+ *   7 sum_rr        sum_i ref_i^2
+ *   8 sum_dr        sum_i d_i ref_i
+ *   9 cos           sum_dr / sqrt(sum_dd * sum_rr)
+ * Maxima compare |x| as binary64 bit patterns (a NaN anywhere gives NaN).
+ * A ratio 0/0 is 0 (an all-zero unit has no error); cos is 1 when both
+ * vectors are zero and 0 when exactly one is. */
+#define ORACLE_STATS 10
+void oracle_error_report(const int8_t *q, const float *scale, const float *ref,
+                         int64_t n, const int64_t *off, int64_t n_units,
+                         double *stats_out);
+
 #ifdef __cplusplus
 }
 #endif

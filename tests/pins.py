@@ -7,7 +7,8 @@ against deliberately broken copies of it (test_oracle_mutants.py).
 
 Method source: the pipelined HCCL AllReduce article
 (bjdmk.com.cn/news/6235379): §2.1 dynamic_chunk, §2.2.1 quantize_gradient
-and the INT8 AllReduce, §6.1 unscale before quantizing.
+and the INT8 AllReduce, §6.1 unscale before quantizing, §5.2 the precision
+check with quantization switched off (fp32 reference sum, error report).
 """
 import json
 import math
@@ -482,5 +483,215 @@ def pin_requantize_is_quantize_of_sum(o):
         assert res["scale_out"][u] == np.float32(s.item())
         assert np.array_equal(res["q_out"][a:b], want.numpy())
 
+
+
+# --------------------------------------------------------------------------
+# §5.2 precision check: the unquantized fp32 sum and the error report
+
+
+def pin_sum_f32_single_rank(o):
+    """W = 1 without the mean: the sum is the loaded gradient itself (+0
+    plus g is g, except -0 which becomes +0)."""
+    rng = np.random.default_rng(20)
+    x = _random_grad(rng, 5000)
+    x[:3] = [0.0, -0.0, np.float32(2.0 ** -149)]
+    r = o.sum_f32([x], F32)
+    want = x.copy()
+    want[1] = 0.0
+    assert np.array_equal(r.view(np.uint32), want.view(np.uint32))
+    h = np.arange(0, 65536, 7, dtype=np.uint16)
+    h = h[np.isfinite(h.view(np.float16))]
+    r = o.sum_f32([h], F16, 2.0 ** -16)
+    want = (h.view(np.float16).astype(np.float64) * 2.0 ** -16).astype(np.float32) + np.float32(0)
+    assert np.array_equal(r, want)
+
+
+def pin_sum_f32_closed_form(o):
+    """Closed form: integer-valued gradients below 2^20 sum exactly in
+    binary32 in any order; W = 4 makes the mean an exact scaling by 1/4."""
+    rng = np.random.default_rng(21)
+    n, W = 4000, 4
+    ints = [rng.integers(-2 ** 20, 2 ** 20, n) for _ in range(W)]
+    xs = [a.astype(np.float32) for a in ints]
+    total = np.sum(ints, axis=0)
+    assert np.array_equal(o.sum_f32(xs, F32), total.astype(np.float32))
+    assert np.array_equal(o.sum_f32(xs, F32, mean=True), (total / 4.0).astype(np.float32))
+
+
+def pin_sum_f32_torch_rank_order(o):
+    """Library routine: torch on the CPU, acc = acc + g_w in rank order, then
+    acc / W (a binary32 division) for the mean."""
+    rng = np.random.default_rng(22)
+    W, n = 7, 30000
+    xs = [_random_grad(rng, n) * np.float32(10.0 ** rng.uniform(-3, 3)) for _ in range(W)]
+    acc = torch.zeros(n, dtype=torch.float32)
+    for x in xs:
+        acc = acc + torch.from_numpy(x)
+    assert np.array_equal(o.sum_f32(xs, F32).view(np.uint32), acc.numpy().view(np.uint32))
+    mean = acc / W
+    assert np.array_equal(o.sum_f32(xs, F32, mean=True).view(np.uint32),
+                          mean.numpy().view(np.uint32))
+    hs = [(x * np.float32(300)).astype(np.float16).view(np.uint16) for x in xs]
+    acc = torch.zeros(n, dtype=torch.float32)
+    for h in hs:
+        acc = acc + torch.from_numpy(h.view(np.float16)).float() * 0.5
+    assert np.array_equal(o.sum_f32(hs, F16, 0.5).view(np.uint32), acc.numpy().view(np.uint32))
+
+
+def pin_golden_sum_f32(o):
+    for ex in _golden()["sum_f32"]:
+        if "x" in ex:
+            xs = [np.array(row, dtype=np.float32) for row in ex["x"]]
+            r = o.sum_f32(xs, F32)
+            assert np.array_equal(r, np.array(ex["r"], dtype=np.float32)), (ex["name"], r)
+            m = o.sum_f32(xs, F32, mean=True)
+            want = np.array([_pow2(a, b) for a, b in zip(ex["mean_r_mult"], ex["mean_r_exp2"])],
+                            dtype=np.float32)
+            assert np.array_equal(m, want), (ex["name"], m)
+        else:
+            hs = [np.array(row, dtype=np.uint16) for row in ex["bits"]]
+            r = o.sum_f32(hs, F16, 2.0 ** -16)
+            want = np.array([_pow2(a, b) for a, b in zip(ex["r_mult"], ex["r_exp2"])],
+                            dtype=np.float32)
+            assert np.array_equal(r, want), (ex["name"], r)
+
+
+def _stat(o_row, name):
+    from oracle import STATS
+    return o_row[STATS.index(name)]
+
+
+def _golden_value(v):
+    if isinstance(v, list):
+        return v[0] / v[1]
+    return float(v)
+
+
+def pin_golden_error_report(o):
+    from oracle import STATS
+    for ex in _golden()["error_report"]:
+        q = np.array(ex["q"], dtype=np.int8)
+        if "scale" in ex:
+            s = np.float32(ex["scale"])
+        else:
+            s = _pow2(ex["scale_mult"], ex["scale_exp2"])
+        ref = np.array([np.nan if v == "nan" else v for v in ex["ref"]], dtype=np.float32)
+        off = np.array([0, q.size], dtype=np.int64)
+        row = o.error_report(q, np.array([s], np.float32), ref, off)[0]
+        for name, v in ex["stats"].items():
+            assert row[STATS.index(name)] == _golden_value(v), (ex["name"], name, row)
+        for name in ex.get("nan_stats", []):
+            assert np.isnan(row[STATS.index(name)]), (ex["name"], name, row)
+
+
+def _exact_d(q, s):
+    """float(q) * s rounded once to binary32 (numpy's binary32 product)."""
+    return (q.astype(np.float32) * np.float32(s)).astype(np.float32)
+
+
+def pin_error_report_identical_and_negated(o):
+    """Closed forms: against itself the INT8 result has zero error and
+    cos = 1 exactly (sqrt of a rounded square returns the value); against
+    its negation the error is twice the values, mean_rel_err = 2 and
+    cos = -1 exactly."""
+    rng = np.random.default_rng(23)
+    n = 20000
+    off = _units(n, rng)
+    q = rng.integers(-128, 128, n).astype(np.int8)
+    sc = (rng.random(off.size - 1) * 1e-3 + 1e-6).astype(np.float32)
+    d = np.concatenate([_exact_d(q[off[u]:off[u + 1]], sc[u]) for u in range(off.size - 1)])
+    rep = o.error_report(q, sc, d, off)
+    for u in range(off.size - 1):
+        row = rep[u]
+        nz = np.any(d[off[u]:off[u + 1]] != 0)
+        assert _stat(row, "max_abs_err") == 0 and _stat(row, "sum_abs_err") == 0, u
+        assert _stat(row, "max_rel_err") == 0 and _stat(row, "mean_rel_err") == 0, u
+        assert _stat(row, "sum_dd") == _stat(row, "sum_rr") == _stat(row, "sum_dr"), u
+        assert _stat(row, "cos") == 1.0, (u, nz)
+    rep = o.error_report(q, sc, -d, off)
+    for u in range(off.size - 1):
+        row = rep[u]
+        seg = d[off[u]:off[u + 1]].astype(np.float64)
+        if not np.any(seg != 0):
+            continue
+        assert _stat(row, "max_abs_err") == 2 * np.max(np.abs(seg)), u
+        assert _stat(row, "max_abs_ref") == np.max(np.abs(seg)), u
+        assert _stat(row, "max_rel_err") == 2.0, u
+        assert _stat(row, "mean_rel_err") == 2.0, u
+        assert _stat(row, "cos") == -1.0, u
+
+
+def pin_error_report_exact_rational(o):
+    """Brute force in exact rational arithmetic on small units: the maxima
+    are the exact maxima rounded to binary64 (rounding is monotone), and
+    every sum lies within gamma_{m+1} * (sum of |terms|) of the exact sum,
+    gamma_k = k u / (1 - k u), u = 2^-53, m the unit length."""
+    rng = np.random.default_rng(24)
+    n = 400
+    off = _units(n, rng, 60)
+    q = rng.integers(-128, 128, n).astype(np.int8)
+    sc = (rng.random(off.size - 1) * 2.0 ** rng.uniform(-20, 20, off.size - 1)).astype(np.float32)
+    ref = np.concatenate([_exact_d(q[off[u]:off[u + 1]], sc[u]) for u in range(off.size - 1)])
+    ref = (ref * (1 + rng.standard_normal(n).astype(np.float32) * np.float32(0.01))
+           + rng.standard_normal(n).astype(np.float32) * np.float32(1e-4)).astype(np.float32)
+    rep = o.error_report(q, sc, ref, off)
+    u53 = Fraction(1, 2 ** 53)
+    for u in range(off.size - 1):
+        a, b = int(off[u]), int(off[u + 1])
+        m = b - a
+        gamma = (m + 1) * u53 / (1 - (m + 1) * u53)
+        d = [Fraction(float(v)) for v in _exact_d(q[a:b], sc[u])]
+        r = [Fraction(float(v)) for v in ref[a:b]]
+        err = [abs(x - y) for x, y in zip(d, r)]
+        row = rep[u]
+        assert _stat(row, "max_abs_err") == float(max(err)), u
+        assert _stat(row, "max_abs_ref") == float(max(abs(y) for y in r)), u
+        exact = {"sum_abs_err": (sum(err), sum(err)),
+                 "sum_abs_ref": (sum(abs(y) for y in r), sum(abs(y) for y in r)),
+                 "sum_dd": (sum(x * x for x in d), sum(x * x for x in d)),
+                 "sum_rr": (sum(y * y for y in r), sum(y * y for y in r)),
+                 "sum_dr": (sum(x * y for x, y in zip(d, r)), sum(abs(x * y) for x, y in zip(d, r)))}
+        for name, (val, mag) in exact.items():
+            assert abs(Fraction(_stat(row, name)) - val) <= gamma * mag, (u, name)
+        cos_exact = float(exact["sum_dr"][0]) / math.sqrt(float(exact["sum_dd"][0]) *
+                                                          float(exact["sum_rr"][0]))
+        assert abs(_stat(row, "cos") - cos_exact) <= 8 * (m + 4) * 2.0 ** -53, u
+        assert abs(_stat(row, "mean_rel_err") - float(exact["sum_abs_err"][0] /
+                                                       exact["sum_abs_ref"][0])) <= \
+            4 * (m + 2) * 2.0 ** -53 * _stat(row, "mean_rel_err"), u
+
+
+def pin_error_report_numpy_scipy(o):
+    """Library routines on larger units: numpy's binary64 max / sum / dot and
+    scipy's cosine distance (1 - cos), within the summation-order bound."""
+    from scipy.spatial.distance import cosine
+    rng = np.random.default_rng(25)
+    W, n = 4, 60000
+    off = _units(n, rng, 9000)
+    xs = [_random_grad(rng, n) for _ in range(W)]
+    res = o.allreduce_step(xs, F32, off)
+    ref = o.sum_f32(xs, F32)
+    rep = o.error_report(res["q_out"], res["scale_out"], ref, off)
+    for u in range(off.size - 1):
+        a, b = off[u], off[u + 1]
+        m = b - a
+        d = _exact_d(res["q_out"][a:b], res["scale_out"][u]).astype(np.float64)
+        r = ref[a:b].astype(np.float64)
+        row = rep[u]
+        tol = 4 * (m + 2) * 2.0 ** -53
+        assert _stat(row, "max_abs_err") == np.max(np.abs(d - r)), u
+        assert _stat(row, "max_abs_ref") == np.max(np.abs(r)), u
+        assert abs(_stat(row, "sum_abs_err") - np.sum(np.abs(d - r))) <= tol * np.sum(np.abs(d - r)), u
+        assert abs(_stat(row, "sum_dr") - np.dot(d, r)) <= tol * np.dot(np.abs(d), np.abs(r)), u
+        assert abs(_stat(row, "sum_rr") - np.dot(r, r)) <= tol * np.dot(r, r), u
+        if np.any(d != 0) and np.any(r != 0):
+            assert abs((1 - _stat(row, "cos")) - cosine(d, r)) <= 1e-12, u
+        # the INT8 result differs from the fp32 sum by at most half a code
+        # step of every rank's quantization and of the requantization, plus
+        # the sums' own rounding: a sanity bound a wrong unit would break
+        steps = res["scale_out"][u] + sum(res["scale"][w][u] for w in range(W))
+        mag = np.max(np.sum([np.abs(x[a:b].astype(np.float64)) for x in xs], axis=0))
+        assert _stat(row, "max_abs_err") <= 0.5 * (1 + 2.0 ** -16) * steps + \
+            2 * W * 2.0 ** -23 * mag, u
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -43,6 +43,23 @@ MUTANTS = [
     ("plan_no_alignment", "int64_t denom = chunk_bytes - chunk_bytes % align_bytes;", "int64_t denom = chunk_bytes;"),
     ("plan_round_count", "int64_t k = nbytes / denom;", "int64_t k = (nbytes + denom - 1) / denom;"),
     ("requantize_with_amax_off_by_one", "float s = oracle_scale(amax[u]);", "float s = oracle_scale(amax[u] + 1);"),
+    ("sum_reverse_order", "for (int32_t rank = 0; rank < W; ++rank) {",
+     "for (int32_t rank = W - 1; rank >= 0; --rank) {"),
+    ("sum_mean_times_recip", "r_out[i] = r_out[i] / (float)W;",
+     "r_out[i] = r_out[i] * (1.0f / (float)W);"),
+    ("sum_skips_unscale", "oracle_load(x[rank], kind, in_mul, n, g);",
+     "oracle_load(x[rank], kind, 1.0f, n, g);"),
+    ("report_dequant_in_double", "double d = (double)((float)q[i] * scale[u]);",
+     "double d = (double)q[i] * (double)scale[u];"),
+    ("report_scale_of_unit0", "double d = (double)((float)q[i] * scale[u]);",
+     "double d = (double)((float)q[i] * scale[0]);"),
+    ("report_signed_ref_sum", "sum_ref = sum_ref + fabs(r);", "sum_ref = sum_ref + r;"),
+    ("report_cos_wrong_norm", "o[9] = dr / sqrt(dd * rr);", "o[9] = dr / sqrt(dd * dd);"),
+    ("report_no_zero_ratio_rule", "    if (a == 0.0 && b == 0.0)\n        return 0.0;\n", ""),
+    ("report_max_ref_of_error", "if (abs_bits(r) > max_ref)\n                max_ref = abs_bits(r);",
+     "if (abs_bits(e) > max_ref)\n                max_ref = abs_bits(e);"),
+    ("report_mean_rel_inverted", "o[5] = ratio_or_zero(sum_err, sum_ref);",
+     "o[5] = ratio_or_zero(sum_ref, sum_err);"),
 ]
 
 
