@@ -448,4 +448,52 @@ gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale
                                                static_cast<hipStream_t>(stream)));
 }
 
+gq_status gq_sum_f32(const void *const *x, int32_t W, gq_dtype dt, float in_mul, int64_t n,
+                     int32_t mean, float *r_out, gq_stream stream) {
+    const char *op = "gq_sum_f32";
+    GQ_TRY(check_ranks(op, W));
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    if (!std::isfinite(in_mul) || !(in_mul > 0.0f))
+        return fail(GQ_ERR_INVALID, op, "in_mul = %g must be finite and > 0", (double)in_mul);
+    if (n < 1 || n > (int64_t{1} << 40))
+        return fail(GQ_ERR_INVALID, op, "n = %lld outside [1, 2^40]", (long long)n);
+    GQ_TRY(check_ptr_array(op, "x", x, W, 16));
+    GQ_TRY(check_ptr(op, "r_out", r_out, 16));
+    gq::SArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int32_t w = 0; w < W; ++w) a.x[w] = x[w];
+    a.r = r_out;
+    a.n = n;
+    a.in_mul = in_mul;
+    a.W = W;
+    a.mean = mean ? 1 : 0;
+    return launch_status(op, gq::launch_sum_f32(a, dt, static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_error_report(const int8_t *q, const float *scale, const float *ref,
+                          const gq_units *u, double *stats_out, gq_stream stream) {
+    const char *op = "gq_error_report";
+    GQ_TRY(check_ptr(op, "q", q, 16));
+    GQ_TRY(check_ptr(op, "scale", scale, 4));
+    GQ_TRY(check_ptr(op, "ref", ref, 16));
+    GQ_TRY(check_ptr(op, "stats_out", stats_out, 8));
+    GQ_TRY(check_units(op, u));
+    const gq::Table &t = u->tab[gq::TAB_R];
+    if (!gq::table_ready(t, u->n_units))
+        return fail(GQ_ERR_INVALID, op, "unit table is incomplete");
+    gq::EArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q;
+    a.scale = scale;
+    a.ref = ref;
+    a.stats = stats_out;
+    a.tiles = t.d_tiles;
+    a.unit_first = t.d_unit_first;
+    a.partial = reinterpret_cast<uint64_t *>(t.d_partial);
+    a.n = u->n;
+    a.n_tiles = t.n_tiles;
+    a.n_units = u->n_units;
+    return launch_status(op, gq::launch_error_report(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -156,9 +156,40 @@ struct RArgs {
     int32_t W;
 };
 
-// Launchers (gq_kernels.hip).  Each returns the first launch error.
+// Arguments of the unquantized reference sum (gq_check.hip).
+struct SArgs {
+    const void *x[GQ_MAX_RANKS];
+    float *r;                   // [n]
+    int64_t n;
+    float in_mul;
+    int32_t W;
+    int32_t mean;
+};
+
+// Arguments of the error report (gq_check.hip).  The per-tile partial
+// statistics live in the reduce table's scratch (d_partial), which holds
+// GQ_MAX_RANKS * 4 bytes per tile; a tile needs kReportWords * 8.
+constexpr int kReportWords = 8;
+static_assert(kReportWords * 8 <= GQ_MAX_RANKS * 4, "report partials fit the tile scratch");
+struct EArgs {
+    const int8_t *q;            // [n]
+    const float *scale;         // [n_units]
+    const float *ref;           // [n]
+    double *stats;              // [n_units][GQ_STATS]
+    const Tile *tiles;          // reduce table tiles, unit order
+    const int32_t *unit_first;  // [n_units + 1]
+    uint64_t *partial;          // [n_tiles][kReportWords]
+    int64_t n;
+    int64_t n_tiles;
+    int64_t n_units;
+};
+
+// Launchers (gq_kernels.hip, gq_check.hip).  Each returns the first launch
+// error.
 hipError_t launch_absmax(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
 hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
 hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, hipStream_t s);
+hipError_t launch_sum_f32(const SArgs &a, gq_dtype dt, hipStream_t s);
+hipError_t launch_error_report(const EArgs &a, hipStream_t s);
 
 }  // namespace gq

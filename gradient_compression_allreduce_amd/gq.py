@@ -23,7 +23,11 @@ CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_faults",
            "gq_absmax", "gq_quantize",
-           "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize")
+           "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
+           "gq_sum_f32", "gq_error_report")
+GQ_STATS = 10
+STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
+         "mean_rel_err", "sum_dd", "sum_rr", "sum_dr", "cos")
 
 
 class GQError(RuntimeError):
@@ -65,6 +69,10 @@ def _load():
     L.gq_requantize.argtypes = [vp, vp, vp, vp, vp]
     L.gq_reduce_requantize.restype = st
     L.gq_reduce_requantize.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+    L.gq_sum_f32.restype = st
+    L.gq_sum_f32.argtypes = [vp, i32, i32, f32, i64, i32, vp, vp]
+    L.gq_error_report.restype = st
+    L.gq_error_report.argtypes = [vp, vp, vp, vp, vp, vp]
     return L
 
 
@@ -91,6 +99,15 @@ def _stream(stream):
     if hasattr(stream, "cuda_stream"):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _need(name, t, numel):
+    """Host-side guard: a contiguous device tensor of at least numel
+    elements (the library reads and writes exactly what the call sizes
+    say)."""
+    if not t.is_cuda or not t.is_contiguous() or t.numel() < numel:
+        raise ValueError("%s must be a contiguous device tensor of at least %d elements"
+                         % (name, numel))
 
 
 def _ptrs(tensors):
@@ -215,3 +232,27 @@ def gq_reduce_requantize(codes, scales, units, scale_out, q_out, r_out=None, str
     rp = r_out.data_ptr() if r_out is not None else None
     _check(lib.gq_reduce_requantize(pq, ps, len(codes), units.handle, rp,
                                     scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))
+
+
+def gq_sum_f32(xs, r_out, in_mul=1.0, mean=False, stream=None):
+    """fp32 rank-order sum of the unquantized gradients xs (divided by W if
+    mean) into r_out (float32, n)."""
+    n = xs[0].numel()
+    for i, x in enumerate(xs):
+        _need("xs[%d]" % i, x, n)
+    _need("r_out", r_out, n)
+    px, keep = _ptrs(xs)
+    _check(lib.gq_sum_f32(px, len(xs), _dtype_code(xs[0]), in_mul, n, 1 if mean else 0,
+                          r_out.data_ptr(), _stream(stream)))
+
+
+def gq_error_report(q, scale, ref, units, stats_out, stream=None):
+    """Per-unit binary64 error statistics of the INT8 result (q, scale)
+    against ref; stats_out: float64 tensor of n_units * GQ_STATS, columns
+    named by STATS."""
+    _need("q", q, units.n)
+    _need("scale", scale, units.n_units)
+    _need("ref", ref, units.n)
+    _need("stats_out", stats_out, units.n_units * GQ_STATS)
+    _check(lib.gq_error_report(q.data_ptr(), scale.data_ptr(), ref.data_ptr(), units.handle,
+                               stats_out.data_ptr(), _stream(stream)))

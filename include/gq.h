@@ -162,8 +162,11 @@ gq_status gq_absmax(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
  * scale = fl32(max|g| / 127); code = clamp(round_half_even(fl32(g / scale)),
  * -128, 127); scale 0 gives codes 0; a NaN quotient gives code 0.
  * x          host array of W device pointers (n elements of dt each).
- * amax_bits  NULL: the maxima are computed here (one fused pass for units
- *            of up to 128 KiB, two passes above that).  Otherwise a device
+ * amax_bits  NULL: the maxima are computed here, fused with the code pass
+ *            (every input read once) for units of up to as many work-group
+ *            tiles as the device keeps resident (16K-37K elements per tile:
+ *            hundreds of millions of elements); larger units take a second
+ *            pass.  Otherwise a device
  *            array [W][n_units] from gq_absmax (or any caller-provided
  *            maxima as bit patterns of non-negative floats).
  * scale_out  host array of W device pointers, each receiving n_units fp32.
@@ -198,14 +201,81 @@ gq_status gq_requantize(const float *r, const gq_units *u, float *scale_out,
 
 /*
  * gq_reduce_requantize -- gq_reduce_dequant followed by gq_requantize,
- * fused: the sum stays on chip for units of up to 128 KiB of fp32 sum (it
- * is recomputed from the codes in a second pass for larger units).
+ * fused: the sum stays on chip for units of up to as many 8192-element
+ * tiles as the device keeps resident (it is recomputed from the codes in a
+ * second pass for larger units).
  * Results are bit-identical to the two separate calls.
  * r_out      NULL, or a device array of n fp32 that also receives the sum.
  */
 gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale,
                                int32_t W, const gq_units *u, float *r_out,
                                float *scale_out, int8_t *q_out, gq_stream stream);
+
+/* ---- Precision check with quantization switched off ----------------------
+ * The article's troubleshooting section (§5.2, gradient anomalies) checks
+ * whether a problem is one of precision by switching gradient quantization
+ * off.  These two calls give that fp32 reference and measure an INT8 result
+ * against it, unit by unit. */
+
+/*
+ * gq_sum_f32 -- the fp32 AllReduce reduction of the unquantized gradients
+ * on one device:
+ *   r[i] = (((+0 + g_0[i]) + g_1[i]) + ...) + g_{W-1}[i],  g_w = float(x_w) * in_mul
+ * each sum rounded to binary32, ranks in order (the same order as the INT8
+ * reduction).  mean != 0 then divides every sum by W (one rounded binary32
+ * division): the averaged gradient of data-parallel training, as in the
+ * torchtitan-npu article's mixed-precision listing, which divides
+ * all-reduced fp32 gradients by the group size.
+ * x      host array of W device pointers, each n elements of dt, 16-byte
+ *        aligned.
+ * n      elements per rank, 1 .. 2^40.  No unit table is needed.
+ * r_out  device array of n fp32, 16-byte aligned, not overlapping x.
+ * Errors: GQ_ERR_INVALID (W, dt, n, in_mul as for gq_absmax; NULL
+ * pointers), GQ_ERR_ALIGN, GQ_ERR_HIP.
+ */
+gq_status gq_sum_f32(const void *const *x, int32_t W, gq_dtype dt, float in_mul, int64_t n,
+                     int32_t mean, float *r_out, gq_stream stream);
+
+/*
+ * gq_error_report -- per-unit statistics, in binary64, of an INT8 result
+ * against an fp32 reference: d[i] = fl32(float(q[i]) * scale[u]) (the value
+ * the codes stand for, one binary32 rounding) and ref[i], over the elements
+ * i of unit u.  GQ_STATS doubles per unit, in the order of GQ_STAT_*:
+ *   MAX_ABS_ERR   max |d - ref|   (the binary64 difference, rounded once)
+ *   MAX_ABS_REF   max |ref|
+ *   MAX_REL_ERR   MAX_ABS_ERR / MAX_ABS_REF
+ *   SUM_ABS_ERR   sum |d - ref|
+ *   SUM_ABS_REF   sum |ref|
+ *   MEAN_REL_ERR  SUM_ABS_ERR / SUM_ABS_REF
+ *   SUM_DD, SUM_RR, SUM_DR   sum d^2, sum ref^2, sum d*ref
+ *   COS           SUM_DR / sqrt(SUM_DD * SUM_RR)   (cosine similarity)
+ * A 0/0 ratio is 0 (a unit with nothing in it has no error); COS is 1 when
+ * d and ref are both zero and 0 when exactly one is.  Maxima compare |x| as
+ * bit patterns, so a NaN anywhere in the unit gives a NaN maximum; NaN and
+ * inf enter the sums by IEEE rules.  The maxima are exact.  The sums are
+ * taken in a fixed order (repeatable bit for bit), not element order: each
+ * lies within 2 (m-1) 2^-53 / (1 - (m-1) 2^-53) of the sum of its terms'
+ * magnitudes from the element-order sum, m the unit's length.
+ * q          device array of n int8 codes, 16-byte aligned.
+ * scale      device array of n_units fp32.
+ * ref        device array of n fp32, 16-byte aligned.
+ * stats_out  device array of n_units * GQ_STATS doubles, 8-byte aligned.
+ * Uses the table's scratch (ordered with other calls on the table).
+ * Errors: GQ_ERR_INVALID, GQ_ERR_ALIGN, GQ_ERR_DEVICE, GQ_ERR_HIP.
+ */
+#define GQ_STAT_MAX_ABS_ERR 0
+#define GQ_STAT_MAX_ABS_REF 1
+#define GQ_STAT_MAX_REL_ERR 2
+#define GQ_STAT_SUM_ABS_ERR 3
+#define GQ_STAT_SUM_ABS_REF 4
+#define GQ_STAT_MEAN_REL_ERR 5
+#define GQ_STAT_SUM_DD 6
+#define GQ_STAT_SUM_RR 7
+#define GQ_STAT_SUM_DR 8
+#define GQ_STAT_COS 9
+#define GQ_STATS 10
+gq_status gq_error_report(const int8_t *q, const float *scale, const float *ref,
+                          const gq_units *u, double *stats_out, gq_stream stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "gq.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gq_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -137,3 +137,36 @@ def test_units_create_rejects_bad_tables(gq):
         assert not h.value
     assert L.gq_units_create(None, 1, ctypes.byref(h)) == gq.GQ_ERR_INVALID
     assert L.gq_units_destroy(None) == gq.GQ_OK
+
+
+def test_check_path_argument_errors(gq):
+    """The quantization-off reference sum and the error report reject bad
+    arguments on the host (no GPU needed)."""
+    L = gq.lib
+    good = 0x10000
+    x = _arr([good] * 3)
+    null = None
+    assert L.gq_sum_f32(x, 0, gq.GQ_F32, 1.0, 100, 0, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_sum_f32(x, 65, gq.GQ_F32, 1.0, 100, 0, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_sum_f32(x, 3, 9, 1.0, 100, 0, good, null) == gq.GQ_ERR_INVALID
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert L.gq_sum_f32(x, 3, gq.GQ_F32, bad, 100, 0, good, null) == gq.GQ_ERR_INVALID
+    for n in (0, -5, (1 << 40) + 1):
+        assert L.gq_sum_f32(x, 3, gq.GQ_F32, 1.0, n, 0, good, null) == gq.GQ_ERR_INVALID
+    assert "n =" in gq.gq_last_error()
+    assert L.gq_sum_f32(_arr([good, 0, good]), 3, gq.GQ_F32, 1.0, 100, 0, good,
+                        null) == gq.GQ_ERR_INVALID
+    assert L.gq_sum_f32(_arr([good, good, good + 8]), 3, gq.GQ_F16, 1.0, 100, 1, good,
+                        null) == gq.GQ_ERR_ALIGN
+    assert L.gq_sum_f32(x, 3, gq.GQ_F32, 1.0, 100, 0, null, null) == gq.GQ_ERR_INVALID
+    assert L.gq_sum_f32(x, 3, gq.GQ_F32, 1.0, 100, 0, good + 4, null) == gq.GQ_ERR_ALIGN
+    assert "r_out" in gq.gq_last_error()
+    # error report: pointers first, then the unit table
+    assert L.gq_error_report(null, good, good, null, good, null) == gq.GQ_ERR_INVALID
+    assert L.gq_error_report(good + 1, good, good, null, good, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_error_report(good, good + 2, good, null, good, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_error_report(good, good, good + 4, null, good, null) == gq.GQ_ERR_ALIGN
+    assert L.gq_error_report(good, good, good, null, good + 4, null) == gq.GQ_ERR_ALIGN
+    assert "stats_out" in gq.gq_last_error()
+    assert L.gq_error_report(good, good, good, null, good, null) == gq.GQ_ERR_INVALID
+    assert "unit table" in gq.gq_last_error()
