@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip the quantization-off comparison (fp32 sum + error report)")
     ap.add_argument("--graph-reps", type=int, default=None,
                     help="also time the step replayed from a HIP graph of this many "
                          "repetitions (default: 100 for the launch-bound 1M-element "
@@ -244,6 +246,40 @@ def main():
     copy_gbps = 2 * cp_src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del cp_src, cp_dst
 
+    ab = None
+    if not args.no_ab:
+        # the precision check with quantization switched off, outside the
+        # timed step: the fp32 rank-order sum of the same gradients and the
+        # per-unit error report of the INT8 result against it
+        ref = torch.empty(w.n, dtype=torch.float32, device=dev)
+        stats = torch.empty(U * gq.GQ_STATS, dtype=torch.float64, device=dev)
+        step()
+        gq.gq_sum_f32(dx, ref, in_mul=w.in_mul, stream=stream)
+        gq.gq_error_report(q_out, s_out, ref, units, stats, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for _ in range(5):
+            gq.gq_sum_f32(dx, ref, in_mul=w.in_mul, stream=stream)
+        e[1].record(stream)
+        for _ in range(5):
+            gq.gq_error_report(q_out, s_out, ref, units, stats, stream=stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        sum_ms = e[0].elapsed_time(e[1]) / 5
+        rep_ms = e[1].elapsed_time(e[2]) / 5
+        st = stats.cpu().numpy().reshape(U, gq.GQ_STATS)
+        col = {k: i for i, k in enumerate(gq.STATS)}
+        fin = np.isfinite(st[:, col["cos"]])
+        ab = {"fp32_sum_ms": round(sum_ms, 4),
+              "fp32_sum_GBps": round((w.W * w.n * w.elem_bytes + 4 * w.n) / (sum_ms * 1e-3) / 1e9, 1),
+              "report_ms": round(rep_ms, 4),
+              "report_GBps": round(5 * w.n / (rep_ms * 1e-3) / 1e9, 1),
+              "units_non_finite": int((~fin).sum()),
+              "worst_max_rel_err": float(np.max(st[fin, col["max_rel_err"]])) if fin.any() else None,
+              "mean_mean_rel_err": float(np.mean(st[fin, col["mean_rel_err"]])) if fin.any() else None,
+              "min_cos": float(np.min(st[fin, col["cos"]])) if fin.any() else None}
+        del ref, stats
+
     input_bytes = w.W * w.n * w.elem_bytes
     value = input_bytes / (ms * 1e-3) / 1e9
     b_alg = bq + br
@@ -279,6 +315,7 @@ def main():
         "step_ms_min": round(float(np.min(step_ms)), 4),
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
         "graph": graph,
+        "ab_fp32": ab,
         # the quantize stage is one launch of the persistent quantize kernel
         "roofline": {"bound": "hbm", "kernel": qkernel,
                      "achieved": round(q_achieved, 1), "peak": HBM_PEAK / 1e9,

@@ -143,6 +143,26 @@ gq::TableId q_table(gq_dtype dt) { return dt == GQ_F32 ? gq::TAB_Q32 : gq::TAB_Q
 
 }  // namespace
 
+// A pipelined step plan: one unit table per bucket, with offsets relative to
+// a 16-element boundary at or before the bucket's first element (so that
+// every per-bucket buffer base stays 16-byte aligned), a second stream, and
+// the events that order the two streams.
+struct gq_pipe {
+    int device = -1;
+    int64_t n = 0;
+    int64_t n_units = 0;
+    int64_t n_buckets = 0;
+    std::vector<int64_t> base;    // element offset of each bucket's tables
+    std::vector<int64_t> u0;      // first unit of each bucket
+    std::vector<gq_units *> tab;  // per-bucket unit tables
+    int64_t slot_elems = 0;
+    int64_t slot_units = 0;
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_q[2] = {nullptr, nullptr};
+    hipEvent_t ev_r[2] = {nullptr, nullptr};
+    hipEvent_t ev_done = nullptr;
+};
+
 extern "C" {
 
 const char *gq_last_error(void) { return g_last_error.c_str(); }
@@ -183,7 +203,7 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
     if (!h_off) return fail(GQ_ERR_INVALID, op, "h_off is NULL");
     if (n_units < 1 || n_units > (int64_t(1) << 30))
         return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
-    if (h_off[0] != 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld, must be 0", (long long)h_off[0]);
+    if (h_off[0] < 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld < 0", (long long)h_off[0]);
     for (int64_t u = 0; u < n_units; ++u)
         if (h_off[u + 1] <= h_off[u])
             return fail(GQ_ERR_INVALID, op, "h_off not strictly increasing at unit %lld",
@@ -409,7 +429,7 @@ gq_status gq_reduce_dequant(const int8_t *const *q, const float *const *scale, i
     a.r = r_out;
     a.faults = u->d_faults;
     a.n = u->n;
-    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], false,
+    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], false, false,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -444,8 +464,160 @@ gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale
     a.n = u->n;
     a.scale_out = scale_out;
     a.q_out = q_out;
-    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], true,
+    return launch_status(op, gq::launch_reduce(a, u->tab[gq::TAB_R], true, false,
                                                static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_pipe_destroy(gq_pipe *p) {
+    if (!p) return ok();
+    for (gq_units *u : p->tab) (void)gq_units_destroy(u);
+    for (int k = 0; k < 2; ++k) {
+        if (p->ev_q[k]) (void)hipEventDestroy(p->ev_q[k]);
+        if (p->ev_r[k]) (void)hipEventDestroy(p->ev_r[k]);
+    }
+    if (p->ev_done) (void)hipEventDestroy(p->ev_done);
+    if (p->aux) (void)hipStreamDestroy(p->aux);
+    delete p;
+    return ok();
+}
+
+gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *bucket_units,
+                         int64_t n_buckets, gq_pipe **out) {
+    const char *op = "gq_pipe_create";
+    if (!out) return fail(GQ_ERR_INVALID, op, "out is NULL");
+    *out = nullptr;
+    if (!h_off || !bucket_units) return fail(GQ_ERR_INVALID, op, "h_off or bucket_units is NULL");
+    if (n_units < 1 || n_units > (int64_t(1) << 30))
+        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
+    if (h_off[0] != 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld, must be 0", (long long)h_off[0]);
+    for (int64_t u = 0; u < n_units; ++u)
+        if (h_off[u + 1] <= h_off[u])
+            return fail(GQ_ERR_INVALID, op, "h_off not strictly increasing at unit %lld", (long long)u);
+    if (h_off[n_units] > (int64_t(1) << 40))
+        return fail(GQ_ERR_INVALID, op, "n = %lld above 2^40", (long long)h_off[n_units]);
+    if (n_buckets < 1 || n_buckets > n_units)
+        return fail(GQ_ERR_INVALID, op, "n_buckets = %lld outside [1, n_units]", (long long)n_buckets);
+    if (bucket_units[0] != 0 || bucket_units[n_buckets] != n_units)
+        return fail(GQ_ERR_INVALID, op, "bucket_units must run from 0 to n_units");
+    for (int64_t b = 0; b < n_buckets; ++b)
+        if (bucket_units[b + 1] <= bucket_units[b])
+            return fail(GQ_ERR_INVALID, op, "bucket_units not strictly increasing at bucket %lld",
+                        (long long)b);
+    gq_pipe *P = new (std::nothrow) gq_pipe;
+    if (!P) return fail(GQ_ERR_INVALID, op, "out of host memory");
+    if (hipGetDevice(&P->device) != hipSuccess) {
+        delete P;
+        return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    }
+    P->n = h_off[n_units];
+    P->n_units = n_units;
+    P->n_buckets = n_buckets;
+    for (int64_t b = 0; b < n_buckets; ++b) {
+        const int64_t ua = bucket_units[b], ub = bucket_units[b + 1];
+        const int64_t base = h_off[ua] & ~int64_t{15};
+        std::vector<int64_t> local(static_cast<size_t>(ub - ua + 1));
+        for (int64_t u = ua; u <= ub; ++u) local[static_cast<size_t>(u - ua)] = h_off[u] - base;
+        gq_units *t = nullptr;
+        const gq_status st = gq_units_create(local.data(), ub - ua, &t);
+        if (st != GQ_OK) {
+            (void)gq_pipe_destroy(P);
+            return st;  // gq_units_create set the error text
+        }
+        P->tab.push_back(t);
+        P->base.push_back(base);
+        P->u0.push_back(ua);
+        P->slot_elems = std::max(P->slot_elems, h_off[ub] - base);
+        P->slot_units = std::max(P->slot_units, ub - ua);
+    }
+    hipError_t e = hipStreamCreateWithFlags(&P->aux, hipStreamNonBlocking);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        e = hipEventCreateWithFlags(&P->ev_q[k], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&P->ev_r[k], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&P->ev_done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)gq_pipe_destroy(P);
+        return fail(GQ_ERR_HIP, op, "stream or event creation failed: %s", hipGetErrorString(e));
+    }
+    *out = P;
+    return ok();
+}
+
+gq_status gq_pipe_slots(const gq_pipe *p, int64_t *slot_elems, int64_t *slot_units) {
+    if (!p) return fail(GQ_ERR_INVALID, "gq_pipe_slots", "plan is NULL");
+    if (slot_elems) *slot_elems = p->slot_elems;
+    if (slot_units) *slot_units = p->slot_units;
+    return ok();
+}
+
+gq_status gq_pipe_faults(const gq_pipe *p, uint64_t *count) {
+    const char *op = "gq_pipe_faults";
+    if (!p) return fail(GQ_ERR_INVALID, op, "plan is NULL");
+    if (!count) return fail(GQ_ERR_INVALID, op, "count is NULL");
+    uint64_t total = 0;
+    for (gq_units *u : p->tab) {
+        uint64_t c = 0;
+        GQ_TRY(gq_units_faults(u, &c));
+        total += c;
+    }
+    *count = total;
+    return ok();
+}
+
+gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                       int8_t *const *q_slot, float *const *scale_slot, float *scale_out,
+                       int8_t *q_out, gq_stream stream) {
+    const char *op = "gq_pipe_step";
+    gq::QArgs qa;
+    GQ_TRY(fill_qargs(op, x, W, dt, in_mul, qa));
+    GQ_TRY(check_ptr_array(op, "q_slot", q_slot, 2 * W, 16));
+    GQ_TRY(check_ptr_array(op, "scale_slot", scale_slot, 2 * W, 4));
+    GQ_TRY(check_ptr(op, "scale_out", scale_out, 4));
+    GQ_TRY(check_ptr(op, "q_out", q_out, 16));
+    if (!p) return fail(GQ_ERR_INVALID, op, "plan is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    if (dev != p->device)
+        return fail(GQ_ERR_DEVICE, op, "current device %d, plan lives on device %d", dev, p->device);
+    const hipStream_t s_main = static_cast<hipStream_t>(stream);
+    const int64_t esz = dt == GQ_F32 ? 4 : 2;
+    for (int64_t b = 0; b < p->n_buckets; ++b) {
+        const int s = static_cast<int>(b & 1);
+        const gq_units *t = p->tab[static_cast<size_t>(b)];
+        const int64_t base = p->base[static_cast<size_t>(b)];
+        // quantize bucket b into slot s (once the reduce of bucket b-2 has
+        // released it)
+        if (b >= 2 && hipStreamWaitEvent(s_main, p->ev_r[s], 0) != hipSuccess)
+            return fail(GQ_ERR_HIP, op, "hipStreamWaitEvent failed");
+        gq::QArgs a = qa;
+        for (int32_t w = 0; w < W; ++w) {
+            a.x[w] = static_cast<const uint8_t *>(x[w]) + base * esz;
+            a.scale[w] = scale_slot[s * W + w];
+            a.q[w] = q_slot[s * W + w];
+        }
+        a.amax = nullptr;
+        GQ_TRY(bind_qtable(op, t, dt, a));
+        hipError_t e = gq::launch_quantize(a, dt, t->tab[q_table(dt)], s_main);
+        if (e == hipSuccess) e = hipEventRecord(p->ev_q[s], s_main);
+        if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_q[s], 0);
+        if (e != hipSuccess) return launch_status(op, e);
+        // reduce + requantize bucket b on the second stream, in the form
+        // whose work groups never wait on each other (it may share the
+        // device with the next bucket's quantize)
+        gq::RArgs r;
+        GQ_TRY(fill_rargs(op, q_slot + s * W, scale_slot + s * W, W, r));
+        r.r = nullptr;
+        r.faults = t->d_faults;
+        r.n = t->n;
+        r.scale_out = scale_out + p->u0[static_cast<size_t>(b)];
+        r.q_out = q_out + base;
+        e = gq::launch_reduce(r, t->tab[gq::TAB_R], true, true, p->aux);
+        if (e == hipSuccess) e = hipEventRecord(p->ev_r[s], p->aux);
+        if (e != hipSuccess) return launch_status(op, e);
+    }
+    hipError_t e = hipEventRecord(p->ev_done, p->aux);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s_main, p->ev_done, 0);
+    return launch_status(op, e);
 }
 
 gq_status gq_sum_f32(const void *const *x, int32_t W, gq_dtype dt, float in_mul, int64_t n,

@@ -188,7 +188,11 @@ struct EArgs {
 // error.
 hipError_t launch_absmax(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
 hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
-hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, hipStream_t s);
+// wait_free: never use the persistent kernel (whose work groups wait on
+// each other); used where another kernel may hold the device's compute
+// units at the same time.
+hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, bool wait_free,
+                         hipStream_t s);
 hipError_t launch_sum_f32(const SArgs &a, gq_dtype dt, hipStream_t s);
 hipError_t launch_error_report(const EArgs &a, hipStream_t s);
 

@@ -102,16 +102,6 @@ __device__ __forceinline__ int code_exact(float g, float s) {
     return (t == t) ? static_cast<int>(r) : 0;
 }
 
-// Code of g for a normal scale s with |g| <= max (so |g/s| <= 128) and
-// r = fl(1/s): see the header comment for why this equals code_exact.
-__device__ __forceinline__ int code_fast(float g, float s, float r) {
-    const float q0 = __fmul_rn(g, r);
-    float c = __builtin_rintf(q0);
-    const float d = fabsf(__fsub_rn(q0, c));
-    if (d >= kNearHalf) c = __builtin_rintf(__fdiv_rn(g, s));
-    return static_cast<int>(c);
-}
-
 // Codes of four values in the fast mode (normal scale, |g| <= max), packed
 // into the four bytes of a word.  Adding 1.5 * 2^23 to q0 = fl(g * r)
 // rounds it to an integer half-to-even (|q0| < 2^22) and leaves that
@@ -368,11 +358,12 @@ __device__ __forceinline__ void store_sum_part(float *r, int64_t i0, int64_t b, 
     }
 }
 
-// Code of one element for a code mode fixed at compile time.
+// Code of one element for the exact and zero modes (the fast mode codes
+// four values at a time, codes4_fast).
 template <int MODE>
 __device__ __forceinline__ int code_of(float g, const QuantParams &p) {
-    if constexpr (MODE == CM_FAST) return code_fast(g, p.s, p.r);
-    else if constexpr (MODE == CM_EXACT) return code_exact(g, p.s);
+    static_assert(MODE != CM_FAST, "the fast mode goes through codes4_fast");
+    if constexpr (MODE == CM_EXACT) return code_exact(g, p.s);
     else return 0;
 }
 
@@ -1211,7 +1202,8 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
     return mul ? quantize_typed<__half, true>(a, t, s) : quantize_typed<__half, false>(a, t, s);
 }
 
-hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipStream_t s) {
+hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,
+                         hipStream_t s) {
     if (!table_ready(t, 1)) return hipErrorInvalidValue;
     RArgs a = a0;
     a.tiles = t.d_tiles;
@@ -1230,7 +1222,7 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipSt
     }
     constexpr auto coop = k_reduce_coop<R_SLOTS, R_BLOCK>;
     const int64_t resident = resident_groups<coop>(R_BLOCK);
-    if (resident >= t.big_max_count) {
+    if (!wait_free && resident >= t.big_max_count) {
         RArgs c = a;
         c.small = t.d_small;
         c.n_small = t.n_small;
@@ -1240,10 +1232,12 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, hipSt
         const int64_t groups = t.n_big > small_groups ? t.n_big : small_groups;
         return launch_persistent(coop, groups < resident ? groups : resident, R_BLOCK, c, s);
     }
-    RArgs p = a;
-    p.list = t.d_multi;
-    hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_PASS1>), dim3(static_cast<unsigned>(t.n_multi)),
-                       block, 0, s, p);
+    if (t.n_multi > 0) {
+        RArgs p = a;
+        p.list = t.d_multi;
+        hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_PASS1>),
+                           dim3(static_cast<unsigned>(t.n_multi)), block, 0, s, p);
+    }
     a.list = nullptr;
     hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
                        block, 0, s, a);

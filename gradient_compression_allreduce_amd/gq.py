@@ -24,7 +24,8 @@ EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_faults",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
-           "gq_sum_f32", "gq_error_report")
+           "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
+           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_step")
 GQ_STATS = 10
 STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
          "mean_rel_err", "sum_dd", "sum_rr", "sum_dr", "cos")
@@ -69,6 +70,16 @@ def _load():
     L.gq_requantize.argtypes = [vp, vp, vp, vp, vp]
     L.gq_reduce_requantize.restype = st
     L.gq_reduce_requantize.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+    L.gq_pipe_create.restype = st
+    L.gq_pipe_create.argtypes = [vp, i64, vp, i64, ctypes.POINTER(vp)]
+    L.gq_pipe_destroy.restype = st
+    L.gq_pipe_destroy.argtypes = [vp]
+    L.gq_pipe_slots.restype = st
+    L.gq_pipe_slots.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.gq_pipe_faults.restype = st
+    L.gq_pipe_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.gq_pipe_step.restype = st
+    L.gq_pipe_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]
     L.gq_sum_f32.restype = st
     L.gq_sum_f32.argtypes = [vp, i32, i32, f32, i64, i32, vp, vp]
     L.gq_error_report.restype = st
@@ -256,3 +267,72 @@ def gq_error_report(q, scale, ref, units, stats_out, stream=None):
     _need("stats_out", stats_out, units.n_units * GQ_STATS)
     _check(lib.gq_error_report(q.data_ptr(), scale.data_ptr(), ref.data_ptr(), units.handle,
                                stats_out.data_ptr(), _stream(stream)))
+
+
+class Pipe:
+    """Owner of a gq_pipe plan (destroyed with the object)."""
+
+    def __init__(self, offsets, bucket_units):
+        off = np.ascontiguousarray(offsets, dtype=np.int64)
+        bu = np.ascontiguousarray(bucket_units, dtype=np.int64)
+        h = ctypes.c_void_p()
+        _check(lib.gq_pipe_create(off.ctypes.data, off.size - 1, bu.ctypes.data, bu.size - 1,
+                                  ctypes.byref(h)))
+        self.handle = h
+        self.n = int(off[-1])
+        self.n_units = off.size - 1
+        self.n_buckets = bu.size - 1
+
+    def close(self):
+        if self.handle:
+            _check(lib.gq_pipe_destroy(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gq_pipe_create(offsets, bucket_units):
+    return Pipe(offsets, bucket_units)
+
+
+def gq_pipe_destroy(pipe):
+    pipe.close()
+
+
+def gq_pipe_slots(pipe):
+    """(slot_elems, slot_units) of one code/scale slot per rank."""
+    e, u = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.gq_pipe_slots(pipe.handle, ctypes.byref(e), ctypes.byref(u)))
+    return e.value, u.value
+
+
+def gq_pipe_faults(pipe):
+    c = ctypes.c_uint64(0)
+    _check(lib.gq_pipe_faults(pipe.handle, ctypes.byref(c)))
+    return c.value
+
+
+def gq_pipe_step(pipe, xs, q_slots, scale_slots, scale_out, q_out, in_mul=1.0, stream=None):
+    """Pipelined step over the plan's buckets.  q_slots / scale_slots: lists
+    of 2*W tensors (slot s of rank w at index s*W + w)."""
+    W = len(xs)
+    se, su = gq_pipe_slots(pipe)
+    if len(q_slots) != 2 * W or len(scale_slots) != 2 * W:
+        raise ValueError("need 2*W code slots and 2*W scale slots")
+    for i, x in enumerate(xs):
+        _need("xs[%d]" % i, x, pipe.n)
+    for i, t in enumerate(q_slots):
+        _need("q_slots[%d]" % i, t, se)
+    for i, t in enumerate(scale_slots):
+        _need("scale_slots[%d]" % i, t, su)
+    _need("scale_out", scale_out, pipe.n_units)
+    _need("q_out", q_out, pipe.n)
+    px, k1 = _ptrs(xs)
+    pq, k2 = _ptrs(q_slots)
+    ps, k3 = _ptrs(scale_slots)
+    _check(lib.gq_pipe_step(pipe.handle, px, W, _dtype_code(xs[0]), in_mul, pq, ps,
+                            scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))

@@ -103,12 +103,13 @@ gq_status gq_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
 
 /*
  * gq_units_create -- build a unit table on the current device.
- * h_off    host array of n_units+1 element offsets: h_off[0] = 0, strictly
+ * h_off    host array of n_units+1 element offsets: h_off[0] >= 0, strictly
  *          increasing; n = h_off[n_units] elements per rank (1 .. 2^40).
  *          Unit u is [h_off[u], h_off[u+1]).  Units may start at any
- *          element offset.  Per-tensor units are the tensors' boundaries in
- *          the flat buffer; per-chunk units concatenate each tensor's
- *          gq_plan_chunks offsets.
+ *          element offset; elements before h_off[0] belong to no unit and
+ *          are neither read into a result nor written.  Per-tensor units
+ *          are the tensors' boundaries in the flat buffer; per-chunk units
+ *          concatenate each tensor's gq_plan_chunks offsets.
  * out      receives the table.
  * Allocates device memory (work tables + scratch, about 1 KiB per 32K
  * elements) and synchronizes the device.  Errors: GQ_ERR_INVALID,
@@ -210,6 +211,71 @@ gq_status gq_requantize(const float *r, const gq_units *u, float *scale_out,
 gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale,
                                int32_t W, const gq_units *u, float *r_out,
                                float *scale_out, int8_t *q_out, gq_stream stream);
+
+/* ---- Two-stream bucket pipeline ------------------------------------------
+ * The article's three-stage pipeline (§2.1, pipeline scheduling) overlaps
+ * the stages of successive gradient blocks with double buffering, and its
+ * tuning parameters (§4.2) set the pipeline depth to 2.  Here the blocks
+ * are buckets (consecutive groups of whole units, such as a data-parallel
+ * job's 25 MiB gradient buckets): bucket b's quantize runs on the caller's
+ * stream into code slot b % 2, and its reduce + requantize runs on a second
+ * stream once that quantize is done, overlapping bucket b+1's quantize;
+ * bucket b+2's quantize waits until bucket b's reduce has released the
+ * slot.  Two slots of codes stand in for the whole model's codes. */
+
+typedef struct gq_pipe gq_pipe;
+
+/*
+ * gq_pipe_create -- plan the pipelined step on the current device.
+ * h_off         n_units+1 unit offsets as for gq_units_create, h_off[0] = 0.
+ * bucket_units  n_buckets+1 unit indices: bucket b is the units
+ *               [bucket_units[b], bucket_units[b+1]); bucket_units[0] = 0,
+ *               strictly increasing, bucket_units[n_buckets] = n_units.
+ * out           receives the plan.
+ * Builds one unit table per bucket, a second stream (default priority) and
+ * the events that order the two; allocates and synchronizes.  Errors:
+ * GQ_ERR_INVALID, GQ_ERR_HIP.
+ */
+gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *bucket_units,
+                         int64_t n_buckets, gq_pipe **out);
+
+/* Free a plan (its work must have completed; NULL is accepted). */
+gq_status gq_pipe_destroy(gq_pipe *p);
+
+/*
+ * gq_pipe_slots -- sizes of one slot: slot_elems int8 codes and slot_units
+ * fp32 scales per rank (a bucket's elements from a 16-element boundary at
+ * or before its first unit, and its unit count, for the largest bucket).
+ */
+gq_status gq_pipe_slots(const gq_pipe *p, int64_t *slot_elems, int64_t *slot_units);
+
+/*
+ * gq_pipe_faults -- bounded waits that gave up in the plan's quantize
+ * launches (see gq_units_faults).  Synchronizes the device.
+ */
+gq_status gq_pipe_faults(const gq_pipe *p, uint64_t *count);
+
+/*
+ * gq_pipe_step -- the whole per-device step (the codes and scales of every
+ * rank, their rank-order reduction and its requantization), bucket by
+ * bucket with the two-slot pipeline above.  scale_out and q_out equal
+ * those of gq_quantize followed by gq_reduce_requantize bit for bit.
+ * x           host array of W device pointers, n elements of dt each,
+ *             16-byte aligned.
+ * q_slot      host array of 2*W device pointers: slot s of rank w is
+ *             q_slot[s*W + w], slot_elems int8, 16-byte aligned.  After the
+ *             call a slot holds the codes of the last bucket that used it,
+ *             from that bucket's 16-element boundary on.
+ * scale_slot  host array of 2*W device pointers, slot_units fp32 each,
+ *             4-byte aligned; likewise the last bucket's scales.
+ * scale_out   device array of n_units fp32.  q_out: device array of n int8.
+ * `stream` waits for all of the step's work before anything later on it
+ * runs.  A launch error after the first bucket leaves earlier buckets'
+ * work enqueued.  Calls sharing a plan must be ordered.
+ */
+gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                       int8_t *const *q_slot, float *const *scale_slot, float *scale_out,
+                       int8_t *q_out, gq_stream stream);
 
 /* ---- Precision check with quantization switched off ----------------------
  * The article's troubleshooting section (§5.2, gradient anomalies) checks

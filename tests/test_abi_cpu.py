@@ -130,7 +130,7 @@ def test_argument_errors_before_any_device_call(gq):
 def test_units_create_rejects_bad_tables(gq):
     L = gq.lib
     h = ctypes.c_void_p()
-    for off in ([0], [1, 5], [0, 5, 5], [0, 5, 3]):
+    for off in ([0], [-1, 5], [0, 5, 5], [0, 5, 3]):
         a = np.array(off, dtype=np.int64)
         st = L.gq_units_create(a.ctypes.data, a.size - 1, ctypes.byref(h))
         assert st == gq.GQ_ERR_INVALID, off
@@ -170,3 +170,34 @@ def test_check_path_argument_errors(gq):
     assert "stats_out" in gq.gq_last_error()
     assert L.gq_error_report(good, good, good, null, good, null) == gq.GQ_ERR_INVALID
     assert "unit table" in gq.gq_last_error()
+
+
+def test_pipe_argument_errors(gq):
+    """The bucket pipeline rejects bad plans and arguments on the host."""
+    L = gq.lib
+    h = ctypes.c_void_p()
+    off = np.array([0, 10, 20, 35], dtype=np.int64)
+    # (valid plans need a device; only the rejections run here)
+    for bu, nb in (([1, 3], 1), ([0, 2], 1), ([0, 2, 2, 3], 3), ([0, 3], 0), ([0, 1, 2, 3, 3], 4)):
+        b = np.array(bu, dtype=np.int64)
+        assert L.gq_pipe_create(off.ctypes.data, 3, b.ctypes.data, nb,
+                                ctypes.byref(h)) == gq.GQ_ERR_INVALID, bu
+        assert not h.value
+    bad_off = np.array([5, 10, 20, 35], dtype=np.int64)
+    b = np.array([0, 3], dtype=np.int64)
+    assert L.gq_pipe_create(bad_off.ctypes.data, 3, b.ctypes.data, 1,
+                            ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_create(off.ctypes.data, 3, None, 1, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_destroy(None) == gq.GQ_OK
+    good = 0x10000
+    x = _arr([good] * 2)
+    slots = _arr([good] * 4)
+    assert L.gq_pipe_step(None, x, 2, gq.GQ_F32, 1.0, slots, slots, good, good,
+                          None) == gq.GQ_ERR_INVALID
+    assert "plan" in gq.gq_last_error()
+    assert L.gq_pipe_step(None, x, 2, gq.GQ_F32, 1.0, _arr([good] * 3 + [good + 4]), slots,
+                          good, good, None) == gq.GQ_ERR_ALIGN
+    assert L.gq_pipe_step(None, x, 2, gq.GQ_F32, 0.0, slots, slots, good, good,
+                          None) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_step(None, x, 2, gq.GQ_F32, 1.0, slots, slots, good, good + 8,
+                          None) == gq.GQ_ERR_ALIGN
