@@ -69,6 +69,30 @@ def unit_offsets(w, plan):
     return np.concatenate(parts)
 
 
+def bucket_bounds(w, plan, bucket_bytes=None):
+    """Unit indices where the gradient buckets start (greedy buckets of
+    whole tensors of bucket_bytes if given, else the workload's own
+    buckets, else 25 MiB), plus the end."""
+    if w.buckets and bucket_bytes is None:
+        groups = w.buckets
+    else:
+        bucket_bytes = bucket_bytes or 25 * 1024 * 1024
+        groups, start, acc = [], 0, 0
+        for t, size in enumerate(w.sizes):
+            b = int(size) * w.elem_bytes
+            if acc > 0 and acc + b > bucket_bytes:
+                groups.append((start, t))
+                start, acc = t, 0
+            acc += b
+        groups.append((start, len(w.sizes)))
+    if w.units == "tensor":
+        first_unit = np.arange(len(w.sizes) + 1)
+    else:
+        counts = [len(plan(int(size), w.elem_bytes)) - 1 for size in w.sizes]
+        first_unit = np.concatenate([[0], np.cumsum(counts)])
+    return np.array([first_unit[a] for a, _ in groups] + [first_unit[-1]], dtype=np.int64)
+
+
 def algorithmic_bytes(W, n, e, U):
     """Bytes the method must move with one read of every input:
     quantize: W*n*e in + W*n codes out + W*U scales out;
@@ -125,6 +149,10 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the two-stream bucket pipeline (outside the step)")
+    ap.add_argument("--bucket-mib", type=float, default=None,
+                    help="pipeline bucket size (default: the workload's buckets, else 25)")
     ap.add_argument("--no-ab", action="store_true",
                     help="skip the quantization-off comparison (fp32 sum + error report)")
     ap.add_argument("--graph-reps", type=int, default=None,
@@ -246,6 +274,50 @@ def main():
     copy_gbps = 2 * cp_src.numel() * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del cp_src, cp_dst
 
+    pipeline = None
+    if args.pipeline:
+        # the two-stream bucket pipeline (two code slots per rank), in both
+        # modes, same inputs, same requantized result
+        bounds = bucket_bounds(w, gq.gq_plan_chunks,
+                               int(args.bucket_mib * 1024 * 1024) if args.bucket_mib else None)
+        pipeline = []
+        for mode, name in ((gq.GQ_PIPE_OVERLAP, "overlap"), (gq.GQ_PIPE_SERIAL, "serial")):
+            pipe = gq.gq_pipe_create(off, bounds, mode)
+            se, su = gq.gq_pipe_slots(pipe)
+            q_slots = [torch.empty(se, dtype=torch.int8, device=dev) for _ in range(2 * w.W)]
+            s_slots = [torch.empty(su, dtype=torch.float32, device=dev) for _ in range(2 * w.W)]
+            p_s_out = torch.empty(U, dtype=torch.float32, device=dev)
+            p_q_out = torch.empty(w.n, dtype=torch.int8, device=dev)
+
+            def pstep():
+                gq.gq_pipe_step(pipe, dx, q_slots, s_slots, p_s_out, p_q_out, in_mul=w.in_mul,
+                                stream=stream)
+
+            for _ in range(args.warmup):
+                pstep()
+            torch.cuda.synchronize()
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            for _ in range(args.steps):
+                pstep()
+            p1.record(stream)
+            torch.cuda.synchronize()
+            if gq.gq_pipe_faults(pipe):
+                print("a bounded cross-group wait gave up in the pipeline: results invalid",
+                      file=sys.stderr)
+                sys.exit(3)
+            step()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(p_q_out, q_out)) and bool(
+                torch.equal(p_s_out.view(torch.int32), s_out.view(torch.int32)))
+            p_ms = p0.elapsed_time(p1) / args.steps
+            pipeline.append({"mode": name, "buckets": int(bounds.size - 1),
+                             "ms_per_step": round(p_ms, 4),
+                             "value": round(w.W * w.n * w.elem_bytes / (p_ms * 1e-3) / 1e9, 2),
+                             "code_slot_bytes_per_rank": int(2 * se),
+                             "same_result_as_step": same})
+            del pipe, q_slots, s_slots, p_s_out, p_q_out
+
     ab = None
     if not args.no_ab:
         # the precision check with quantization switched off, outside the
@@ -315,6 +387,7 @@ def main():
         "step_ms_min": round(float(np.min(step_ms)), 4),
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
         "graph": graph,
+        "pipeline": pipeline,
         "ab_fp32": ab,
         # the quantize stage is one launch of the persistent quantize kernel
         "roofline": {"bound": "hbm", "kernel": qkernel,

@@ -157,6 +157,7 @@ struct gq_pipe {
     std::vector<gq_units *> tab;  // per-bucket unit tables
     int64_t slot_elems = 0;
     int64_t slot_units = 0;
+    int32_t mode = GQ_PIPE_OVERLAP;
     hipStream_t aux = nullptr;
     hipEvent_t ev_q[2] = {nullptr, nullptr};
     hipEvent_t ev_r[2] = {nullptr, nullptr};
@@ -482,10 +483,12 @@ gq_status gq_pipe_destroy(gq_pipe *p) {
 }
 
 gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *bucket_units,
-                         int64_t n_buckets, gq_pipe **out) {
+                         int64_t n_buckets, int32_t mode, gq_pipe **out) {
     const char *op = "gq_pipe_create";
     if (!out) return fail(GQ_ERR_INVALID, op, "out is NULL");
     *out = nullptr;
+    if (mode != GQ_PIPE_OVERLAP && mode != GQ_PIPE_SERIAL)
+        return fail(GQ_ERR_INVALID, op, "unknown mode %d", mode);
     if (!h_off || !bucket_units) return fail(GQ_ERR_INVALID, op, "h_off or bucket_units is NULL");
     if (n_units < 1 || n_units > (int64_t(1) << 30))
         return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
@@ -512,6 +515,7 @@ gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *b
     P->n = h_off[n_units];
     P->n_units = n_units;
     P->n_buckets = n_buckets;
+    P->mode = mode;
     for (int64_t b = 0; b < n_buckets; ++b) {
         const int64_t ua = bucket_units[b], ub = bucket_units[b + 1];
         const int64_t base = h_off[ua] & ~int64_t{15};
@@ -580,6 +584,8 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
     if (dev != p->device)
         return fail(GQ_ERR_DEVICE, op, "current device %d, plan lives on device %d", dev, p->device);
     const hipStream_t s_main = static_cast<hipStream_t>(stream);
+    const bool serial = p->mode == GQ_PIPE_SERIAL;
+    const hipStream_t s_red = serial ? s_main : p->aux;
     const int64_t esz = dt == GQ_F32 ? 4 : 2;
     for (int64_t b = 0; b < p->n_buckets; ++b) {
         const int s = static_cast<int>(b & 1);
@@ -587,7 +593,7 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         const int64_t base = p->base[static_cast<size_t>(b)];
         // quantize bucket b into slot s (once the reduce of bucket b-2 has
         // released it)
-        if (b >= 2 && hipStreamWaitEvent(s_main, p->ev_r[s], 0) != hipSuccess)
+        if (!serial && b >= 2 && hipStreamWaitEvent(s_main, p->ev_r[s], 0) != hipSuccess)
             return fail(GQ_ERR_HIP, op, "hipStreamWaitEvent failed");
         gq::QArgs a = qa;
         for (int32_t w = 0; w < W; ++w) {
@@ -598,8 +604,10 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         a.amax = nullptr;
         GQ_TRY(bind_qtable(op, t, dt, a));
         hipError_t e = gq::launch_quantize(a, dt, t->tab[q_table(dt)], s_main);
-        if (e == hipSuccess) e = hipEventRecord(p->ev_q[s], s_main);
-        if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_q[s], 0);
+        if (!serial) {
+            if (e == hipSuccess) e = hipEventRecord(p->ev_q[s], s_main);
+            if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_q[s], 0);
+        }
         if (e != hipSuccess) return launch_status(op, e);
         // reduce + requantize bucket b on the second stream, in the form
         // whose work groups never wait on each other (it may share the
@@ -611,10 +619,11 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         r.n = t->n;
         r.scale_out = scale_out + p->u0[static_cast<size_t>(b)];
         r.q_out = q_out + base;
-        e = gq::launch_reduce(r, t->tab[gq::TAB_R], true, true, p->aux);
-        if (e == hipSuccess) e = hipEventRecord(p->ev_r[s], p->aux);
+        e = gq::launch_reduce(r, t->tab[gq::TAB_R], true, !serial, s_red);
+        if (!serial && e == hipSuccess) e = hipEventRecord(p->ev_r[s], p->aux);
         if (e != hipSuccess) return launch_status(op, e);
     }
+    if (serial) return ok();
     hipError_t e = hipEventRecord(p->ev_done, p->aux);
     if (e == hipSuccess) e = hipStreamWaitEvent(s_main, p->ev_done, 0);
     return launch_status(op, e);

@@ -17,6 +17,7 @@ SO = os.path.join(HERE, "_lib", "libgq.so")
 GQ_OK, GQ_ERR_INVALID, GQ_ERR_ALIGN, GQ_ERR_CAPACITY, GQ_ERR_HIP, GQ_ERR_DEVICE = range(6)
 GQ_F32, GQ_F16 = 0, 1
 GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
+GQ_PIPE_OVERLAP, GQ_PIPE_SERIAL = 0, 1
 GQ_MAX_RANKS = 64
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
@@ -71,7 +72,7 @@ def _load():
     L.gq_reduce_requantize.restype = st
     L.gq_reduce_requantize.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
     L.gq_pipe_create.restype = st
-    L.gq_pipe_create.argtypes = [vp, i64, vp, i64, ctypes.POINTER(vp)]
+    L.gq_pipe_create.argtypes = [vp, i64, vp, i64, i32, ctypes.POINTER(vp)]
     L.gq_pipe_destroy.restype = st
     L.gq_pipe_destroy.argtypes = [vp]
     L.gq_pipe_slots.restype = st
@@ -272,12 +273,12 @@ def gq_error_report(q, scale, ref, units, stats_out, stream=None):
 class Pipe:
     """Owner of a gq_pipe plan (destroyed with the object)."""
 
-    def __init__(self, offsets, bucket_units):
+    def __init__(self, offsets, bucket_units, mode=GQ_PIPE_OVERLAP):
         off = np.ascontiguousarray(offsets, dtype=np.int64)
         bu = np.ascontiguousarray(bucket_units, dtype=np.int64)
         h = ctypes.c_void_p()
         _check(lib.gq_pipe_create(off.ctypes.data, off.size - 1, bu.ctypes.data, bu.size - 1,
-                                  ctypes.byref(h)))
+                                  mode, ctypes.byref(h)))
         self.handle = h
         self.n = int(off[-1])
         self.n_units = off.size - 1
@@ -295,8 +296,8 @@ class Pipe:
             pass
 
 
-def gq_pipe_create(offsets, bucket_units):
-    return Pipe(offsets, bucket_units)
+def gq_pipe_create(offsets, bucket_units, mode=GQ_PIPE_OVERLAP):
+    return Pipe(offsets, bucket_units, mode)
 
 
 def gq_pipe_destroy(pipe):

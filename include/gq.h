@@ -231,13 +231,19 @@ typedef struct gq_pipe gq_pipe;
  * bucket_units  n_buckets+1 unit indices: bucket b is the units
  *               [bucket_units[b], bucket_units[b+1]); bucket_units[0] = 0,
  *               strictly increasing, bucket_units[n_buckets] = n_units.
+ * mode          GQ_PIPE_OVERLAP: the two streams above.  GQ_PIPE_SERIAL:
+ *               every stage on the caller's stream, bucket after bucket
+ *               (no overlap; the reduce may then use its persistent form,
+ *               and reads each bucket's codes soon after they were written).
  * out           receives the plan.
  * Builds one unit table per bucket, a second stream (default priority) and
  * the events that order the two; allocates and synchronizes.  Errors:
  * GQ_ERR_INVALID, GQ_ERR_HIP.
  */
+#define GQ_PIPE_OVERLAP 0
+#define GQ_PIPE_SERIAL 1
 gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *bucket_units,
-                         int64_t n_buckets, gq_pipe **out);
+                         int64_t n_buckets, int32_t mode, gq_pipe **out);
 
 /* Free a plan (its work must have completed; NULL is accepted). */
 gq_status gq_pipe_destroy(gq_pipe *p);

@@ -180,14 +180,17 @@ def test_pipe_argument_errors(gq):
     # (valid plans need a device; only the rejections run here)
     for bu, nb in (([1, 3], 1), ([0, 2], 1), ([0, 2, 2, 3], 3), ([0, 3], 0), ([0, 1, 2, 3, 3], 4)):
         b = np.array(bu, dtype=np.int64)
-        assert L.gq_pipe_create(off.ctypes.data, 3, b.ctypes.data, nb,
+        assert L.gq_pipe_create(off.ctypes.data, 3, b.ctypes.data, nb, 0,
                                 ctypes.byref(h)) == gq.GQ_ERR_INVALID, bu
         assert not h.value
     bad_off = np.array([5, 10, 20, 35], dtype=np.int64)
     b = np.array([0, 3], dtype=np.int64)
-    assert L.gq_pipe_create(bad_off.ctypes.data, 3, b.ctypes.data, 1,
+    assert L.gq_pipe_create(bad_off.ctypes.data, 3, b.ctypes.data, 1, 0,
                             ctypes.byref(h)) == gq.GQ_ERR_INVALID
-    assert L.gq_pipe_create(off.ctypes.data, 3, None, 1, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_create(off.ctypes.data, 3, None, 1, 0, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_create(off.ctypes.data, 3, b.ctypes.data, 1, 7,
+                            ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    assert "mode" in gq.gq_last_error()
     assert L.gq_pipe_destroy(None) == gq.GQ_OK
     good = 0x10000
     x = _arr([good] * 2)

@@ -59,11 +59,16 @@ def run_pipe(gq, pipe, xs, W, in_mul, n, U, reps=1, fresh=None):
             [t.cpu().numpy() for t in s_slots])
 
 
-def check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh=None):
+def check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh=None, mode=None):
+    if mode is None:
+        for m in (gq.GQ_PIPE_OVERLAP, gq.GQ_PIPE_SERIAL):
+            check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh, m)
+        return
+    label = "%s/mode%d" % (label, mode)
     W = len(xs)
     n = int(off[-1])
     U = off.size - 1
-    pipe = gq.gq_pipe_create(off, bounds)
+    pipe = gq.gq_pipe_create(off, bounds, mode)
     final = fresh if fresh is not None else xs
     want = oracle.allreduce_step(final, kind, off, in_mul)
     say("pipeline", label, "W", W, "n", n, "units", U, "buckets", bounds.size - 1)
