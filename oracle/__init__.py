@@ -8,8 +8,9 @@ A thin ctypes wrapper over liboracle.so (oracle.c, plain single-threaded C,
 built with -O2 -ffp-contract=off).  Each function follows one step of the
 pipelined HCCL AllReduce article (bjdmk.com.cn/news/6235379): §2.1 chunk
 plan, §2.2.1 absmax scale / int8 codes / INT8 AllReduce reduction, §6.1
-unscale on load, and §5.2's check with quantization switched off (the fp32
-reference sum and the per-unit error report).
+unscale on load, §5.2's check with quantization switched off (the fp32
+reference sum and the per-unit error report), and §6.2's adaptive chunk
+size.
 """
 import ctypes
 import os
@@ -64,6 +65,8 @@ def _declare(L):
     L.oracle_reduce_dequant.argtypes = [vp, vp, i32, i64, vp, i64, vp]
     L.oracle_requantize.restype = None
     L.oracle_requantize.argtypes = [vp, i64, vp, i64, vp, vp]
+    L.oracle_chunker_predict.restype = i64
+    L.oracle_chunker_predict.argtypes = [vp, vp, i64, i32, ctypes.c_double, i64]
     L.oracle_sum_f32.restype = None
     L.oracle_sum_f32.argtypes = [vp, i32, f32, i32, i64, i32, vp]
     L.oracle_error_report.restype = None
@@ -211,3 +214,11 @@ class Oracle:
         self.L.oracle_error_report(q.ctypes.data, scale.ctypes.data, ref.ctypes.data, n,
                                    off.ctypes.data, U, out.ctypes.data)
         return out
+
+    def chunker_predict(self, sizes, lat, capacity=100, alpha=0.25, default_bytes=131072):
+        """Predicted chunk size after the observations (sizes[i], lat[i])."""
+        sizes = np.ascontiguousarray(sizes, dtype=np.int64)
+        lat = np.ascontiguousarray(lat, dtype=np.float64)
+        assert sizes.size == lat.size
+        return int(self.L.oracle_chunker_predict(sizes.ctypes.data, lat.ctypes.data, sizes.size,
+                                                 capacity, alpha, default_bytes))

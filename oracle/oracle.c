@@ -311,3 +311,44 @@ void oracle_error_report(const int8_t *q, const float *scale, const float *ref,
             o[9] = dr / sqrt(dd * rr);
     }
 }
+
+/* §6.2 DynamicChunker: history of the last `capacity` observations, a
+ * per-size exponentially weighted moving average of latency per byte, the
+ * size with the lowest average (see oracle.h for the reading). */
+int64_t oracle_chunker_predict(const int64_t *sizes, const double *lat, int64_t count,
+                               int32_t capacity, double alpha, int64_t default_bytes)
+{
+    int64_t first = count > capacity ? count - capacity : 0;
+    int64_t best_size = default_bytes;
+    double best_cost = 0.0;
+    int have_best = 0;
+    for (int64_t i = first; i < count; ++i) {
+        int64_t c = sizes[i];
+        int seen_before = 0;
+        for (int64_t j = first; j < i; ++j)
+            if (sizes[j] == c)
+                seen_before = 1;
+        if (seen_before)
+            continue;
+        /* the average of size c over the history, oldest first */
+        double e = 0.0;
+        int started = 0;
+        for (int64_t j = i; j < count; ++j) {
+            if (sizes[j] != c)
+                continue;
+            double x = lat[j] / (double)c;
+            if (!started) {
+                e = x;
+                started = 1;
+            } else {
+                e = alpha * x + (1.0 - alpha) * e;
+            }
+        }
+        if (!have_best || e < best_cost || (e == best_cost && c > best_size)) {
+            best_cost = e;
+            best_size = c;
+            have_best = 1;
+        }
+    }
+    return best_size;
+}

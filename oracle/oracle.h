@@ -121,6 +121,22 @@ void oracle_error_report(const int8_t *q, const float *scale, const float *ref,
                          int64_t n, const int64_t *off, int64_t n_units,
                          double *stats_out);
 
+/* ---- Adaptive chunk size (§6.2 adaptive chunking) -------------------------
+ * The article keeps the last 100 (chunk size, latency) observations and
+ * predicts the best chunk size from them with an exponentially weighted
+ * moving average; the prediction step itself is not printed.  Reading
+ * taken here: each observation's cost is its latency per byte of chunk;
+ * for every chunk size present in the history, the costs of that size are
+ * averaged in history order (oldest first) as e = alpha * x + (1 - alpha) * e,
+ * starting from the first such cost; the size with the smallest average
+ * wins, ties going to the larger size; an empty history gives the default.
+ *
+ * sizes[i], lat[i] for i < count are all observations in arrival order;
+ * only the last `capacity` of them form the history.  All arithmetic is
+ * binary64, one rounding per operation. */
+int64_t oracle_chunker_predict(const int64_t *sizes, const double *lat, int64_t count,
+                               int32_t capacity, double alpha, int64_t default_bytes);
+
 #ifdef __cplusplus
 }
 #endif

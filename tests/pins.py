@@ -8,7 +8,8 @@ against deliberately broken copies of it (test_oracle_mutants.py).
 Method source: the pipelined HCCL AllReduce article
 (bjdmk.com.cn/news/6235379): §2.1 dynamic_chunk, §2.2.1 quantize_gradient
 and the INT8 AllReduce, §6.1 unscale before quantizing, §5.2 the precision
-check with quantization switched off (fp32 reference sum, error report).
+check with quantization switched off (fp32 reference sum, error report),
+§6.2 the adaptive chunk size.
 """
 import json
 import math
@@ -693,5 +694,80 @@ def pin_error_report_numpy_scipy(o):
         mag = np.max(np.sum([np.abs(x[a:b].astype(np.float64)) for x in xs], axis=0))
         assert _stat(row, "max_abs_err") <= 0.5 * (1 + 2.0 ** -16) * steps + \
             2 * W * 2.0 ** -23 * mag, u
+
+
+# --------------------------------------------------------------------------
+# §6.2 adaptive chunk size
+
+
+def pin_golden_chunker(o):
+    for ex in _golden()["chunker"]:
+        if "predict" in ex:
+            for a, want in ex["predict"].items():
+                got = o.chunker_predict(ex["sizes"], ex["lat"], alpha=float(a))
+                assert got == want, (ex["name"], a, got)
+        for cap, want in ex.get("predict_capacity", {}).items():
+            got = o.chunker_predict(ex["sizes"], ex["lat"], capacity=int(cap), alpha=ex["alpha"])
+            assert got == want, (ex["name"], cap, got)
+
+
+def pin_chunker_defaults_and_single_size(o):
+    """No observation gives the default; a single observed size is always
+    the prediction, whatever its latencies."""
+    assert o.chunker_predict([], []) == 131072
+    assert o.chunker_predict([], [], default_bytes=4096) == 4096
+    rng = np.random.default_rng(30)
+    for _ in range(20):
+        k = int(rng.integers(1, 150))
+        c = int(rng.integers(1, 1 << 22))
+        assert o.chunker_predict([c] * k, rng.random(k) * 10 + 1e-3) == c
+
+
+def pin_chunker_constant_costs(o):
+    """Closed form: when every observation of a size costs the same per
+    byte, its average is that cost, so the prediction is the size with the
+    smallest cost (ties to the larger size), for any alpha and any order."""
+    rng = np.random.default_rng(31)
+    for _ in range(40):
+        m = int(rng.integers(2, 7))
+        sizes = [int(v) for v in rng.choice(np.arange(1, 64), m, replace=False) * 16384]
+        cost = {c: float(rng.integers(1, 6)) * 2.0 ** -20 for c in sizes}   # exact values
+        seq = [sizes[int(i)] for i in rng.integers(0, m, 80)]
+        lat = [cost[c] * c for c in seq]
+        present = set(seq)
+        want = min(present, key=lambda c: (cost[c], -c))
+        for alpha in (0.25, 0.5, 1.0, 0.1):
+            assert o.chunker_predict(seq, lat, alpha=alpha) == want
+
+
+def pin_chunker_exact_closed_form(o):
+    """Brute force in exact rational arithmetic: the average of a size with
+    costs x_1..x_k (oldest first) is (1-a)^(k-1) x_1 + sum_{j>=2} a (1-a)^(k-j) x_j;
+    the exact minimiser must be the prediction whenever it is not within
+    1e-9 of the runner-up (a gap no rounding of these short sums reaches)."""
+    rng = np.random.default_rng(32)
+    checked = 0
+    for _ in range(300):
+        m = int(rng.integers(1, 5))
+        sizes = [int(v) * 4096 for v in rng.choice(np.arange(1, 40), m, replace=False)]
+        n_obs = int(rng.integers(1, 25))
+        cap = int(rng.integers(1, 30))
+        seq = [sizes[int(i)] for i in rng.integers(0, m, n_obs)]
+        lat = [float(v) for v in rng.random(n_obs) * 5 + 0.01]
+        alpha = [0.25, 0.5, 0.1, 0.75][int(rng.integers(0, 4))]
+        a = Fraction(alpha)
+        hist = list(zip(seq, lat))[-cap:]
+        avg = {}
+        for c in dict.fromkeys(s for s, _ in hist):
+            xs = [Fraction(l) / c for s, l in hist if s == c]
+            k = len(xs)
+            avg[c] = (1 - a) ** (k - 1) * xs[0] + sum(a * (1 - a) ** (k - j) * xs[j - 1]
+                                                      for j in range(2, k + 1))
+        ranked = sorted(avg.items(), key=lambda kv: (kv[1], -kv[0]))
+        if len(ranked) > 1 and abs(ranked[1][1] - ranked[0][1]) <= Fraction(1, 10 ** 9) * ranked[0][1]:
+            continue
+        assert o.chunker_predict(seq, lat, capacity=cap, alpha=alpha) == ranked[0][0], (seq, lat, cap)
+        checked += 1
+    assert checked > 200
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

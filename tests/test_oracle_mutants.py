@@ -60,6 +60,16 @@ MUTANTS = [
      "if (abs_bits(e) > max_ref)\n                max_ref = abs_bits(e);"),
     ("report_mean_rel_inverted", "o[5] = ratio_or_zero(sum_err, sum_ref);",
      "o[5] = ratio_or_zero(sum_ref, sum_err);"),
+    ("chunker_no_capacity", "int64_t first = count > capacity ? count - capacity : 0;",
+     "int64_t first = 0;"),
+    ("chunker_alpha_swapped", "e = alpha * x + (1.0 - alpha) * e;",
+     "e = (1.0 - alpha) * x + alpha * e;"),
+    ("chunker_tie_to_smaller", "(e == best_cost && c > best_size)", "(e == best_cost && c < best_size)"),
+    ("chunker_raw_latency", "double x = lat[j] / (double)c;", "double x = lat[j];"),
+    ("chunker_start_from_zero", "                e = x;\n                started = 1;",
+     "                e = alpha * x;\n                started = 1;"),
+    ("chunker_capacity_off_by_one", "int64_t first = count > capacity ? count - capacity : 0;",
+     "int64_t first = count > capacity ? count - capacity + 1 : 0;"),
 ]
 
 
