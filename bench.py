@@ -153,6 +153,9 @@ def main():
                     help="also time the two-stream bucket pipeline (outside the step)")
     ap.add_argument("--bucket-mib", type=float, default=None,
                     help="pipeline bucket size (default: the workload's buckets, else 25)")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="per-chunk workloads: feed the adaptive chunker with steps timed "
+                         "at chunk sizes of 32 KiB .. 1 MiB and report its choice")
     ap.add_argument("--no-ab", action="store_true",
                     help="skip the quantization-off comparison (fp32 sum + error report)")
     ap.add_argument("--graph-reps", type=int, default=None,
@@ -318,6 +321,49 @@ def main():
                              "same_result_as_step": same})
             del pipe, q_slots, s_slots, p_s_out, p_q_out
 
+    adaptive = None
+    if args.adaptive and w.units == "chunk":
+        # the adaptive chunker fed with measured steps at several chunk
+        # sizes (each size is its own plan: other chunks, other scales)
+        ch = gq.gq_chunker_create()
+        cands = []
+        for kib in (32, 64, 128, 256, 512, 1024):
+            cb = kib * 1024
+            parts = [np.zeros(1, dtype=np.int64)]
+            for t, size in enumerate(w.sizes):
+                parts.append(gq.gq_plan_chunks(int(size), w.elem_bytes, cb)[1:] + w.toff[t])
+            off_c = np.concatenate(parts)
+            units_c = gq.gq_units_create(off_c)
+            Uc = off_c.size - 1
+            sc_c = [torch.empty(Uc, dtype=torch.float32, device=dev) for _ in range(w.W)]
+            so_c = torch.empty(Uc, dtype=torch.float32, device=dev)
+
+            def cstep():
+                gq.gq_quantize(dx, units_c, sc_c, codes, in_mul=w.in_mul, stream=stream)
+                gq.gq_reduce_requantize(codes, sc_c, units_c, so_c, q_out, stream=stream)
+
+            for _ in range(2):
+                cstep()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for _ in range(5):
+                cstep()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            if gq.gq_units_faults(units_c):
+                print("a bounded cross-group wait gave up: results invalid", file=sys.stderr)
+                sys.exit(3)
+            c_ms = c0.elapsed_time(c1) / 5
+            gq.gq_chunker_update(ch, cb, c_ms * 1e-3 / Uc)   # seconds per chunk
+            cands.append({"chunk_bytes": cb, "chunks": int(Uc), "ms_per_step": round(c_ms, 4)})
+            del units_c, sc_c, so_c
+        pred = gq.gq_chunker_predict(ch)
+        adaptive = {"candidates": cands, "predicted_chunk_bytes": pred,
+                    "ms_at_prediction": next(c["ms_per_step"] for c in cands
+                                             if c["chunk_bytes"] == pred),
+                    "ms_at_128KiB": next(c["ms_per_step"] for c in cands
+                                         if c["chunk_bytes"] == 131072)}
+
     ab = None
     if not args.no_ab:
         # the precision check with quantization switched off, outside the
@@ -388,6 +434,7 @@ def main():
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
         "graph": graph,
         "pipeline": pipeline,
+        "adaptive_chunk": adaptive,
         "ab_fp32": ab,
         # the quantize stage is one launch of the persistent quantize kernel
         "roofline": {"bound": "hbm", "kernel": qkernel,

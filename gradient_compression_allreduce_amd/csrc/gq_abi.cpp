@@ -166,6 +166,15 @@ struct gq_pipe {
 
 extern "C" {
 
+// Error reporting for the library's other host files (hidden, not part of
+// the ABI): GQ_OK clears the text.
+__attribute__((visibility("hidden"))) gq_status gq_set_error_internal(gq_status code,
+                                                                      const char *op,
+                                                                      const char *what) {
+    if (code == GQ_OK) return ok();
+    return fail(code, op, "%s", what);
+}
+
 const char *gq_last_error(void) { return g_last_error.c_str(); }
 
 const char *gq_version(void) { return "gq 0.1 (gfx950)"; }

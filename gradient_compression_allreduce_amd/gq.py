@@ -26,7 +26,8 @@ EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
-           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_step")
+           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_step", "gq_chunker_create",
+           "gq_chunker_destroy", "gq_chunker_update", "gq_chunker_predict", "gq_chunker_plan")
 GQ_STATS = 10
 STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
          "mean_rel_err", "sum_dd", "sum_rr", "sum_dr", "cos")
@@ -81,6 +82,16 @@ def _load():
     L.gq_pipe_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
     L.gq_pipe_step.restype = st
     L.gq_pipe_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.gq_chunker_create.restype = st
+    L.gq_chunker_create.argtypes = [i32, ctypes.c_double, i64, ctypes.POINTER(vp)]
+    L.gq_chunker_destroy.restype = st
+    L.gq_chunker_destroy.argtypes = [vp]
+    L.gq_chunker_update.restype = st
+    L.gq_chunker_update.argtypes = [vp, i64, ctypes.c_double]
+    L.gq_chunker_predict.restype = st
+    L.gq_chunker_predict.argtypes = [vp, ctypes.POINTER(i64)]
+    L.gq_chunker_plan.restype = st
+    L.gq_chunker_plan.argtypes = [vp, i64, i32, vp, i64, ctypes.POINTER(i64)]
     L.gq_sum_f32.restype = st
     L.gq_sum_f32.argtypes = [vp, i32, i32, f32, i64, i32, vp, vp]
     L.gq_error_report.restype = st
@@ -337,3 +348,53 @@ def gq_pipe_step(pipe, xs, q_slots, scale_slots, scale_out, q_out, in_mul=1.0, s
     ps, k3 = _ptrs(scale_slots)
     _check(lib.gq_pipe_step(pipe.handle, px, W, _dtype_code(xs[0]), in_mul, pq, ps,
                             scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))
+
+
+class Chunker:
+    """Owner of a gq_chunker (adaptive chunk size)."""
+
+    def __init__(self, capacity=100, alpha=0.25, default_bytes=CHUNK_BYTES):
+        h = ctypes.c_void_p()
+        _check(lib.gq_chunker_create(capacity, alpha, default_bytes, ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _check(lib.gq_chunker_destroy(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gq_chunker_create(capacity=100, alpha=0.25, default_bytes=CHUNK_BYTES):
+    return Chunker(capacity, alpha, default_bytes)
+
+
+def gq_chunker_destroy(chunker):
+    chunker.close()
+
+
+def gq_chunker_update(chunker, chunk_bytes, latency):
+    _check(lib.gq_chunker_update(chunker.handle, int(chunk_bytes), float(latency)))
+
+
+def gq_chunker_predict(chunker):
+    v = ctypes.c_int64(0)
+    _check(lib.gq_chunker_predict(chunker.handle, ctypes.byref(v)))
+    return v.value
+
+
+def gq_chunker_plan(chunker, numel, elem_bytes):
+    """Chunk offsets of dynamic_chunk with the predicted chunk size."""
+    cnt = ctypes.c_int64(0)
+    st = lib.gq_chunker_plan(chunker.handle, numel, elem_bytes, None, 0, ctypes.byref(cnt))
+    if st != GQ_ERR_CAPACITY:
+        _check(st)
+    off = np.empty(cnt.value + 1, dtype=np.int64)
+    _check(lib.gq_chunker_plan(chunker.handle, numel, elem_bytes, off.ctypes.data, off.size,
+                               ctypes.byref(cnt)))
+    return off

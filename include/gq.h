@@ -283,6 +283,44 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
                        int8_t *const *q_slot, float *const *scale_slot, float *scale_out,
                        int8_t *q_out, gq_stream stream);
 
+/* ---- Adaptive chunk size -------------------------------------------------
+ * The article's adaptive chunking (§6.2) keeps the last 100 (chunk size,
+ * latency) observations and predicts the best chunk size from them with an
+ * exponentially weighted moving average; the prediction step is not
+ * printed.  Reading taken here: an observation's cost is its latency per
+ * byte of chunk; for every chunk size in the history, the costs of that
+ * size are averaged in arrival order as e = alpha*x + (1-alpha)*e, starting
+ * from the first such cost (binary64, one rounding per operation); the size
+ * with the lowest average is predicted, ties going to the larger size; an
+ * empty history predicts the default.  A different chunk size gives
+ * different chunks and, with per-chunk scales, different codes: callers opt
+ * in by planning with gq_chunker_plan.  Host only; calls on one chunker
+ * must not overlap. */
+
+typedef struct gq_chunker gq_chunker;
+
+/* capacity: history length (the article: 100), 1 .. 2^20.  alpha: weight
+ * of the newest cost, in (0, 1].  default_bytes: prediction of an empty
+ * history (the article's 128 KiB), >= 1.  Errors: GQ_ERR_INVALID. */
+gq_status gq_chunker_create(int32_t capacity, double alpha, int64_t default_bytes,
+                            gq_chunker **out);
+
+/* Free a chunker (NULL is accepted). */
+gq_status gq_chunker_destroy(gq_chunker *c);
+
+/* Record one observation: a chunk of chunk_bytes (>= 1) took latency
+ * seconds (finite, >= 0).  The oldest observation leaves a full history.
+ * Errors: GQ_ERR_INVALID. */
+gq_status gq_chunker_update(gq_chunker *c, int64_t chunk_bytes, double latency);
+
+/* The predicted chunk size in bytes (host pointer). */
+gq_status gq_chunker_predict(const gq_chunker *c, int64_t *chunk_bytes);
+
+/* gq_plan_chunks with the predicted chunk size and the article's 64-byte
+ * alignment term (same outputs and errors). */
+gq_status gq_chunker_plan(const gq_chunker *c, int64_t numel, int32_t elem_bytes,
+                          int64_t *off_out, int64_t cap, int64_t *count_out);
+
 /* ---- Precision check with quantization switched off ----------------------
  * The article's troubleshooting section (§5.2, gradient anomalies) checks
  * whether a problem is one of precision by switching gradient quantization
