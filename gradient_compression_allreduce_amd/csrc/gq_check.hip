@@ -12,13 +12,14 @@
 //                      HBM-bound: W*n*e bytes in, 4n out.
 //   k_report_tiles     per-tile binary64 statistics of an INT8 result
 //                      d = fl32(float(q) * s) against an fp32 reference.
-//   k_report_finalize  per-unit combination of the tiles, in tile order,
-//                      and the derived ratios and cosine.
+//   k_report_finalize  per-unit combination of the tiles (one wave per
+//                      unit, fixed order) and the derived ratios and cosine.
 //
 // The report's maxima are exact (a binary64 difference of two binary32
 // values is rounded once, and rounding is monotone); its sums are taken in
 // a fixed order (per lane, then a butterfly over the wave, then waves in
-// order, then tiles in order), so they repeat bit for bit from run to run.
+// order; per unit, tiles strided over a wave's lanes, then a butterfly),
+// so they repeat bit for bit from run to run.
 #include <hip/hip_fp16.h>
 
 #include "gq_internal.h"
@@ -260,40 +261,45 @@ __device__ __forceinline__ double ratio_or_zero(double x, double y) {
     return (x == 0.0 && y == 0.0) ? 0.0 : __ddiv_rn(x, y);
 }
 
-// One lane per unit: its tiles' statistics in tile order, then the ratios
-// (0/0 is 0) and the cosine (1 for two zero vectors, 0 for one).
+// One wave per unit: lane l combines the unit's tiles l, l + 64, ... in
+// order, the wave butterfly combines the lanes (every lane ends with the
+// same totals), then lane 0 takes the ratios (0/0 is 0) and the cosine (1
+// for two zero vectors, 0 for one).  The order is fixed, so the result
+// repeats bit for bit.
 __global__ __launch_bounds__(256) void k_report_finalize(const EArgs a) {
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (u >= a.n_units) return;
+    const int lane = threadIdx.x & 63;
     const int32_t t0 = a.unit_first[u], t1 = a.unit_first[u + 1];
-    uint64_t max_err = 0, max_ref = 0;
-    double err = 0.0, ref = 0.0, dd = 0.0, rr = 0.0, dr = 0.0;
-    for (int32_t t = t0; t < t1; ++t) {
+    Stats st{0, 0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int32_t t = t0 + lane; t < t1; t += 64) {
         const uint64_t *p = a.partial + static_cast<int64_t>(t) * kReportWords;
-        max_err = umax64(max_err, p[0]);
-        max_ref = umax64(max_ref, p[1]);
-        err = __dadd_rn(err, __longlong_as_double(static_cast<long long>(p[2])));
-        ref = __dadd_rn(ref, __longlong_as_double(static_cast<long long>(p[3])));
-        dd = __dadd_rn(dd, __longlong_as_double(static_cast<long long>(p[4])));
-        rr = __dadd_rn(rr, __longlong_as_double(static_cast<long long>(p[5])));
-        dr = __dadd_rn(dr, __longlong_as_double(static_cast<long long>(p[6])));
+        st.max_err = umax64(st.max_err, p[0]);
+        st.max_ref = umax64(st.max_ref, p[1]);
+        st.err = __dadd_rn(st.err, __longlong_as_double(static_cast<long long>(p[2])));
+        st.ref = __dadd_rn(st.ref, __longlong_as_double(static_cast<long long>(p[3])));
+        st.dd = __dadd_rn(st.dd, __longlong_as_double(static_cast<long long>(p[4])));
+        st.rr = __dadd_rn(st.rr, __longlong_as_double(static_cast<long long>(p[5])));
+        st.dr = __dadd_rn(st.dr, __longlong_as_double(static_cast<long long>(p[6])));
     }
+    wave_stats(st);
+    if (lane != 0) return;
     double *o = a.stats + u * GQ_STATS;
-    const double me = __longlong_as_double(static_cast<long long>(max_err));
-    const double mr = __longlong_as_double(static_cast<long long>(max_ref));
+    const double me = __longlong_as_double(static_cast<long long>(st.max_err));
+    const double mr = __longlong_as_double(static_cast<long long>(st.max_ref));
     o[GQ_STAT_MAX_ABS_ERR] = me;
     o[GQ_STAT_MAX_ABS_REF] = mr;
     o[GQ_STAT_MAX_REL_ERR] = ratio_or_zero(me, mr);
-    o[GQ_STAT_SUM_ABS_ERR] = err;
-    o[GQ_STAT_SUM_ABS_REF] = ref;
-    o[GQ_STAT_MEAN_REL_ERR] = ratio_or_zero(err, ref);
-    o[GQ_STAT_SUM_DD] = dd;
-    o[GQ_STAT_SUM_RR] = rr;
-    o[GQ_STAT_SUM_DR] = dr;
+    o[GQ_STAT_SUM_ABS_ERR] = st.err;
+    o[GQ_STAT_SUM_ABS_REF] = st.ref;
+    o[GQ_STAT_MEAN_REL_ERR] = ratio_or_zero(st.err, st.ref);
+    o[GQ_STAT_SUM_DD] = st.dd;
+    o[GQ_STAT_SUM_RR] = st.rr;
+    o[GQ_STAT_SUM_DR] = st.dr;
     double c;
-    if (dd == 0.0 && rr == 0.0) c = 1.0;
-    else if (dd == 0.0 || rr == 0.0) c = 0.0;
-    else c = __ddiv_rn(dr, __dsqrt_rn(__dmul_rn(dd, rr)));
+    if (st.dd == 0.0 && st.rr == 0.0) c = 1.0;
+    else if (st.dd == 0.0 || st.rr == 0.0) c = 0.0;
+    else c = __ddiv_rn(st.dr, __dsqrt_rn(__dmul_rn(st.dd, st.rr)));
     o[GQ_STAT_COS] = c;
 }
 
@@ -324,7 +330,7 @@ hipError_t launch_error_report(const EArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_report_tiles, dim3(static_cast<unsigned>(a.n_tiles)), dim3(REPORT_BLOCK),
                        0, s, a);
-    const int64_t groups = (a.n_units + 255) / 256;
+    const int64_t groups = (a.n_units + 3) / 4;   // one wave per unit
     hipLaunchKernelGGL(k_report_finalize, dim3(static_cast<unsigned>(groups)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
