@@ -54,6 +54,8 @@ def compare_report(got, want, q, scale, ref, off, label):
     m = np.diff(off).astype(np.float64)
     u = 2.0 ** -53
     g = 2 * (m - 1) * u / (1 - (m - 1) * u)
+    start = int(off[0])            # elements before the first unit take no part
+    q, ref, off = q[start:int(off[-1])], ref[start:int(off[-1])], off - start
     seg = np.repeat(np.arange(U), np.diff(off))
     d = (q.astype(np.float32) * scale[seg]).astype(np.float64)
     r = ref.astype(np.float64)

@@ -292,3 +292,34 @@ def test_graph_replays_match_eager(gq, oracle):
         compare_step(other.host(), oracle.allreduce_step(step_xs, F32, off), W,
                      label="eager%d" % rep)
     del g
+
+
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+def test_units_on_tile_boundaries(gq, oracle, kind):
+    """Units of exactly one, two and three tiles of each geometry (16384 and
+    36864 fp32, 32768 and 73728 fp16 elements for the quantize, 8192 for the
+    reduce), and one element more and less, at offsets on and off the
+    16-byte slots."""
+    rng = np.random.default_rng(51 + kind)
+    base = [8192, 16384, 32768, 36864, 73728]
+    lens = []
+    for b in base:
+        for m in (1, 2, 3):
+            lens += [b * m - 1, b * m, b * m + 1]
+    lens = [v for v in lens if v > 0]
+    rng.shuffle(lens)
+    lens = [3] + lens      # shift every later unit off the 16-element grid
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(3)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "tile_bounds_k%d" % kind)
+
+
+def test_fp16_sixty_four_ranks(gq, oracle):
+    """The largest rank count with loss-scaled fp16 inputs."""
+    rng = np.random.default_rng(61)
+    n = 50_003
+    off = _offsets(rng, n, 500, 30_000)
+    xs = [_grad(rng, n, F16) for _ in range(64)]
+    _run_and_compare(gq, oracle, xs, F16, off, 2.0 ** -16, "f16_W64", modes=("fused",))

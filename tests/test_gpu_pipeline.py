@@ -125,7 +125,23 @@ def test_table_starting_past_zero(gq, oracle):
         want_t = dict(want, q=[trim(a) for a in want["q"]], r=trim(want["r"]),
                       q_out=trim(want["q_out"]))
         compare_step(got_t, want_t, 3, check_r=True, label="offset_table_k%d" % kind)
+        # the error report and the fp32 reference on the same table
+        ref = oracle.sum_f32(xs, kind, in_mul)
+        stats = torch.full((U_of(off) * gq.GQ_STATS,), float("nan"), dtype=torch.float64,
+                           device="cuda")
+        gq.gq_error_report(step.q_out, step.scale_out, torch.from_numpy(ref).cuda(), step.units,
+                           stats)
+        torch.cuda.synchronize()
+        got_rep = stats.cpu().numpy().reshape(U_of(off), gq.GQ_STATS)
+        want_rep = oracle.error_report(got["q_out"], got["scale_out"], ref, off)
+        from tests.test_gpu_check import compare_report
+        compare_report(got_rep, want_rep, got["q_out"], got["scale_out"], ref, off,
+                       "offset_report_k%d" % kind)
     torch.cuda.synchronize()
+
+
+def U_of(off):
+    return off.size - 1
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
