@@ -428,6 +428,9 @@ def main():
                    "buckets": len(w.buckets) if w.buckets else None,
                    "seed": args.seed},
         "hbm_fraction": round(b_alg / (ms * 1e-3) / HBM_PEAK, 4),
+        # bytes a rank would exchange (int8 codes + fp32 scales) over the
+        # bytes of its fp32 gradient: the compression of the INT8 AllReduce
+        "wire_bytes_vs_fp32": round((w.n + 4 * U) / (4.0 * w.n), 5),
         "algorithmic_bytes_per_step": b_alg,
         "step_ms_median": round(float(np.median(step_ms)), 4),
         "step_ms_min": round(float(np.min(step_ms)), 4),
