@@ -11,8 +11,9 @@
 //
 // The hot path is one persistent kernel per stage, launched with no more
 // work groups (G) than the device keeps resident at once.  Work groups take
-// tiles in order from a ticket counter (tickets run over ranks, then tiles
-// in unit order), so the tiles of one unit start at about the same time.  A
+// tiles in order from a ticket counter (tickets run over rank 0's tiles in
+// unit order, then rank 1's, and so on), so the tiles of one unit start at
+// about the same time.  A
 // unit larger than one tile combines its tiles' maxima in device memory
 // (see "cross-work-group max" below) and each of its tiles waits, bounded,
 // for the others, so every input byte is read from HBM once.  A work group
@@ -24,9 +25,13 @@
 // fits on the device, so every work group eventually runs (as soon as any
 // other work on the device has finished) and the wait ends for units of up
 // to G tiles.  Larger units take a two-launch fallback (per-tile maxima,
-// then a re-reading quantize pass).  Every wait is bounded: if one ever
-// gives up (the device did not run the grid), a fault counter records it
-// and the launch's results are invalid.
+// then a re-reading quantize pass).  The argument needs the other work on
+// the device to finish without waiting on this grid: two such persistent
+// kernels side by side could each hold compute units the other needs, so
+// where two stages may overlap (the bucket pipeline) one of them runs in
+// its wait-free form.  Every wait is bounded: if one ever gives up (the
+// device did not run the grid), a fault counter records it and the
+// launch's results are invalid.
 //
 // Numerics (must match the CPU oracle bit for bit):
 //   * g = x * in_mul is one rounded binary32 multiply (skipped when
@@ -1028,9 +1033,11 @@ void k_reduce_coop(const RArgs a) {
 
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
 
-// Non-persistent reduce: the plain sum (R_SUM), and the two-launch fallback
-// for units with more tiles than resident work groups (R_PASS1 writes
-// per-tile maxima, R_FUSED recomputes the sum and requantizes).
+// Non-persistent reduce: the plain sum (R_SUM), and the two-launch form
+// whose work groups never wait on each other (R_PASS1 writes per-tile
+// maxima, R_FUSED recomputes the sum and requantizes), used for units with
+// more tiles than resident work groups and where another kernel may share
+// the device.
 template <int S, int BLOCK, int MODE>
 __global__ __launch_bounds__(BLOCK) void k_reduce(const RArgs a) {
     __shared__ uint32_t sh[BLOCK / 64];

@@ -128,7 +128,8 @@ gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
  * gq_units_schedule -- which schedule the fused quantize of a table uses for
  * elements of type dt: GQ_SCHED_LAYER (units spanning many work-group
  * tiles: per-tensor or per-layer scales) or GQ_SCHED_CHUNK (most elements
- * in units of at most one 128 KiB tile: per-chunk scales, small tensors).
+ * in units of at most one 144 KiB tile, which holds a 128 KiB chunk of
+ * every tensor of 1 MiB or more: per-chunk scales, small tensors).
  * Chosen when the table is created; results do not depend on it.
  */
 #define GQ_SCHED_LAYER 0
