@@ -145,7 +145,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -215,58 +215,6 @@ def main():
         gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # the timed region: exactly K steps, nothing else enqueued between them
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    ms = total_ms / args.steps
-    # a second pass with events around each stage (the breakdown, and the
-    # dominant kernel's launch duration for the roofline)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    r_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-
-    graph = None
-    if args.graph_reps > 0:
-        # the same step, captured once into a HIP graph of graph_reps
-        # repetitions (launch-bound workloads); no allocation or memset is
-        # recorded: the library's compute calls make none
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for _ in range(args.graph_reps):
-                    gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=cap)
-                    gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=cap)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        g.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph = {"reps": args.graph_reps,
-                 "ms_per_step": round(g0.elapsed_time(g1) / args.graph_reps, 4)}
-        del g
 
     # practical ceiling: a plain device-to-device copy of the same volume
     bq, br = algorithmic_bytes(w.W, w.n, w.elem_bytes, U)
@@ -403,6 +351,58 @@ def main():
               "mean_mean_rel_err": float(np.mean(st[fin, col["mean_rel_err"]])) if fin.any() else None,
               "min_cos": float(np.min(st[fin, col["cos"]])) if fin.any() else None}
         del ref, stats
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # the timed region: exactly K steps, nothing else enqueued between them
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    # a second pass with events around each stage (the breakdown, and the
+    # dominant kernel's launch duration for the roofline)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    r_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+
+    graph = None
+    if args.graph_reps > 0:
+        # the same step, captured once into a HIP graph of graph_reps
+        # repetitions (launch-bound workloads); no allocation or memset is
+        # recorded: the library's compute calls make none
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(args.graph_reps):
+                    gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=cap)
+                    gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"reps": args.graph_reps,
+                 "ms_per_step": round(g0.elapsed_time(g1) / args.graph_reps, 4)}
+        del g
 
     input_bytes = w.W * w.n * w.elem_bytes
     value = input_bytes / (ms * 1e-3) / 1e9
