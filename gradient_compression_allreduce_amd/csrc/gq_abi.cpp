@@ -53,12 +53,17 @@ void build_tiles(const std::vector<int64_t> &off, int V, int64_t cap_slots,
             tiles.push_back({a, b, static_cast<int32_t>(u), first, 1, -1});
             continue;
         }
+        // as few tiles as the capacity allows, of sizes differing by at
+        // most one slot (so that no tile of the unit is a sliver the others
+        // wait on): tile m starts at slot floor(m * slots / cnt)
         const int64_t cnt = (slots + cap_slots - 1) / cap_slots;
+        const int64_t q = slots / cnt, r = slots % cnt;
+        auto start = [&](int64_t m) { return first_slot + m * q + (m * r) / cnt; };
         const int32_t slot = static_cast<int32_t>(n_multi_units++);
         if (cnt > max_count) max_count = static_cast<int32_t>(cnt);
         for (int64_t m = 0; m < cnt; ++m) {
-            const int64_t sb = (first_slot + m * cap_slots) * V;
-            const int64_t se = (first_slot + (m + 1) * cap_slots) * V;
+            const int64_t sb = start(m) * V;
+            const int64_t se = start(m + 1) * V;
             multi.push_back(static_cast<int32_t>(tiles.size()));
             tiles.push_back({sb > a ? sb : a, se < b ? se : b, static_cast<int32_t>(u), first,
                              static_cast<int32_t>(cnt), slot});
