@@ -206,15 +206,9 @@ def main():
     q_out = torch.empty(w.n, dtype=torch.int8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     # practical ceiling: a plain device-to-device copy of the same volume
     bq, br = algorithmic_bytes(w.W, w.n, w.elem_bytes, U)
@@ -356,28 +350,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # the timed region: exactly K steps, nothing else enqueued between them
+    # the timed region: exactly K steps; an event before and after each
+    # step's quantize launch gives that kernel's duration (the roofline) and
+    # the stage breakdown without extra passes
+    e_q0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e_q1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        e_q0[k].record(stream)
+        gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=stream)
+        e_q1[k].record(stream)
+        gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    # a second pass with events around each stage (the breakdown, and the
-    # dominant kernel's launch duration for the roofline)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    r_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    nxt = e_q0[1:] + [end]
+    q_ms = float(np.mean([e_q0[k].elapsed_time(e_q1[k]) for k in range(args.steps)]))
+    r_ms = float(np.mean([e_q1[k].elapsed_time(nxt[k]) for k in range(args.steps)]))
+    step_ms = [e_q0[k].elapsed_time(nxt[k]) for k in range(args.steps)]
 
     graph = None
     if args.graph_reps > 0:
