@@ -87,6 +87,25 @@ def test_workload_sampled_units(gq, oracle, cfg):
     assert torch.equal(s_out_bench.view(torch.int32), step.scale_out.view(torch.int32))
     del dx
 
+    # properties of every unit at full size (the formula's: the element of
+    # largest magnitude codes to +-127, and with a normal scale no code is
+    # -128), for every rank and for the requantized sum
+    lo = np.float32(2.0 ** -126)
+
+    def check_all_units(codes_dev, scale_host, label):
+        q = codes_dev.cpu().numpy()
+        amax = np.maximum.reduceat(np.abs(q.astype(np.int16)), off[:-1])
+        normal = (scale_host >= lo) & np.isfinite(scale_host)
+        assert np.all(amax[normal] == 127), (label, np.flatnonzero(amax[normal] != 127)[:5])
+        has_min = np.maximum.reduceat((q == -128).astype(np.int8), off[:-1]) > 0
+        assert not np.any(has_min & normal), (label, "code -128 with a normal scale")
+        assert np.all(scale_host[~normal] == 0), (label, "non-normal scale")
+
+    for r in range(w.W):
+        check_all_units(step.codes[r], step.scales[r].cpu().numpy(), "rank %d" % r)
+    check_all_units(step.q_out, step.scale_out.cpu().numpy(), "q_out")
+    say("  every unit: max|code| = 127, no -128")
+
     rng = np.random.default_rng(cfg)
     sample = set(int(u) for u in rng.choice(U, 40, replace=False)) | {0, U - 1}
     if cfg == 3:
