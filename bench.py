@@ -165,7 +165,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the simulated ranks all live in one device's "
-              "memory and this build has no multi-GPU exchange; run with --gpus 1",
+              "memory and the library has no multi-GPU exchange; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

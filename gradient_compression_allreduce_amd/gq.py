@@ -41,7 +41,7 @@ class GQError(RuntimeError):
 
 def _load():
     if not os.path.exists(SO):
-        raise ImportError("libgq.so is not built (%s); run __graft_entry__.build() or "
+        raise ImportError("libgq.so is not built (%s); build it with "
                           "python gradient_compression_allreduce_amd/build.py" % SO)
     L = ctypes.CDLL(SO)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
