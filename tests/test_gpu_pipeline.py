@@ -200,3 +200,17 @@ def test_pipeline_resnet152_buckets(gq, oracle):
     bounds = np.array([a for a, _ in w.buckets] + [len(w.sizes)], dtype=np.int64)
     xs = [w.fill(r) for r in range(w.W)]
     check_pipe(gq, oracle, xs, F32, off, bounds, w.in_mul, w.name)
+
+
+def test_pipeline_tiny_and_odd_buckets(gq, oracle):
+    """Buckets of one element, buckets that start and end inside a 16-byte
+    slot, a bucket with a unit larger than any tile, and more buckets than
+    slots can hold at once."""
+    rng = np.random.default_rng(440)
+    sizes = [1, 3, 17, 1, 40_000, 5, 1, 33, 100_001, 2, 7, 16, 16, 15]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    bounds = np.array([0, 1, 2, 4, 5, 6, 9, 10, 12, 13, 14], dtype=np.int64)
+    for kind in (F32, F16):
+        xs = [_grad(rng, int(off[-1]), kind) for _ in range(3)]
+        in_mul = 2.0 ** -16 if kind == F16 else 1.0
+        check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, "tiny_odd_k%d" % kind)
