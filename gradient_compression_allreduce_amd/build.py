@@ -53,5 +53,22 @@ def build(verbose=False):
     return SO
 
 
+def build_abi_check(verbose=False):
+    """The tests' C++ driver of the C ABI (tests/c_abi), linked against
+    libgq.so."""
+    root = os.path.dirname(HERE)
+    src = os.path.join(root, "tests", "c_abi", "abi_step.cpp")
+    out = os.path.join(root, "tests", "c_abi", "libabi_step.so")
+    if not os.path.exists(src):
+        return None
+    cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-shared", "-x", "hip",
+           "--offload-arch=" + ARCH, src, "-o", out, "-L", LIBDIR, "-lgq",
+           "-Wl,-rpath," + LIBDIR, "-Wl,-rpath,$ORIGIN/../../gradient_compression_allreduce_amd/_lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
