@@ -40,7 +40,17 @@
  *     work runs.  The library never allocates in the compute calls.
  *   - A unit table holds scratch memory: calls that use the same table must
  *     be ordered (same stream, or ordered by events); calls on different
- *     tables may overlap.
+ *     tables may be enqueued on different streams.
+ *   - gq_quantize (fused form), gq_reduce_requantize and gq_pipe_step run
+ *     persistent kernels, whose work groups wait for each other.  Such a
+ *     call must not run at the same time as another one of them on the same
+ *     device (nor beside any other kernel whose work groups wait on each
+ *     other): enqueue them on one stream, or order the streams with events.
+ *     Two of them side by side could each hold compute units the other
+ *     needs; their waits then give up after about a second, the tables'
+ *     fault counters (gq_units_faults) record it, and those calls' outputs
+ *     are invalid.  gq_pipe_step's own two streams are safe: its reduce
+ *     runs in a form that never waits.
  *   - Non-finite inputs follow IEEE arithmetic (see above); there is no
  *     error for them.
  */
