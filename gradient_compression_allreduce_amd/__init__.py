@@ -11,4 +11,4 @@ from .gq import (  # noqa: F401
     gq_pipe_create, gq_pipe_destroy, gq_pipe_faults, gq_pipe_slots, gq_pipe_step,
     gq_plan_chunks, gq_quantize, gq_reduce_dequant, gq_reduce_requantize, gq_requantize,
     gq_sum_f32, gq_units_create, gq_units_destroy, gq_units_faults, gq_units_info,
-    gq_units_schedule, gq_version)
+    gq_units_reduce_tile, gq_units_schedule, gq_version)

@@ -244,9 +244,18 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             64 * static_cast<int64_t>(ti == gq::TAB_R ? gq::SMALL_SLOTS_R : gq::SMALL_SLOTS_Q);
         auto span = [&](int64_t u) { return (off[u + 1] + V - 1) / V - off[u] / V; };
         if (ti == gq::TAB_R) {
+            // wide tiles when most elements of the non-small units sit in
+            // units wider than a narrow tile
+            const int64_t narrow = static_cast<int64_t>(gq::R_BLOCK) * gq::R_SLOTS_NARROW;
+            int64_t in_wide = 0, in_big = 0;
+            for (int64_t u = 0; u < n_units; ++u) {
+                if (span(u) <= small_cap) continue;
+                in_big += off[u + 1] - off[u];
+                if (span(u) > narrow) in_wide += off[u + 1] - off[u];
+            }
             t.sched = gq::SCHED_LAYER;
             t.block = gq::R_BLOCK;
-            t.slots = gq::R_SLOTS;
+            t.slots = (2 * in_wide >= in_big) ? gq::R_SLOTS_WIDE : gq::R_SLOTS_NARROW;
         } else {
             // chunk schedule when most elements of the non-small units sit
             // in units of one chunk tile
@@ -341,6 +350,15 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched) {
     if (!sched) return fail(GQ_ERR_INVALID, op, "sched is NULL");
     if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
     *sched = u->tab[q_table(dt)].sched;
+    return ok();
+}
+
+gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems) {
+    const char *op = "gq_units_reduce_tile";
+    if (!u) return fail(GQ_ERR_INVALID, op, "unit table is NULL");
+    if (!elems) return fail(GQ_ERR_INVALID, op, "elems is NULL");
+    const gq::Table &t = u->tab[gq::TAB_R];
+    *elems = static_cast<int64_t>(t.block) * t.slots * gq::kSlotElems[gq::TAB_R];
     return ok();
 }
 

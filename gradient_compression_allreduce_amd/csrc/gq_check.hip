@@ -30,11 +30,9 @@ namespace {
 constexpr int SUM_BLOCK = 256;
 constexpr int SUM_SLOTS = 2;      // 16-byte input slots per lane and rank group
 constexpr int SUM_RG = 8;         // ranks loaded together
-constexpr int REPORT_BLOCK = R_BLOCK;  // one 16-element slot per lane: a reduce tile
+constexpr int REPORT_BLOCK = R_BLOCK;  // one work group per reduce-table tile
 constexpr int REPORT_V = 16;
 constexpr uint64_t kAbs64 = 0x7fffffffffffffffull;
-
-static_assert(R_SLOTS == 1, "a reduce-table tile is one slot per lane of REPORT_BLOCK");
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t b) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
@@ -179,16 +177,17 @@ __device__ __forceinline__ void wave_stats(Stats &s) {
     }
 }
 
-// One reduce-table tile per work group, one 16-element slot per lane.  The
-// codes and the reference are 16-byte aligned buffers of n elements, so
-// every slot but the buffer's last is read with whole 16-byte loads.
+// One reduce-table tile per work group; lane l takes the tile's 16-element
+// slots l, l + REPORT_BLOCK, ... in order (one slot per lane for a narrow
+// tile, two for a wide one).  The codes and the reference are 16-byte
+// aligned buffers of n elements, so every slot but the buffer's last is
+// read with whole 16-byte loads.
 __global__ __launch_bounds__(REPORT_BLOCK) void k_report_tiles(const EArgs a) {
     __shared__ Stats sh[REPORT_BLOCK / 64];
     const Tile t = a.tiles[blockIdx.x];
-    const int64_t j = t.begin / REPORT_V + threadIdx.x;
     const int64_t j1 = (t.end + REPORT_V - 1) / REPORT_V;
     Stats st{0, 0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    if (j < j1) {
+    for (int64_t j = t.begin / REPORT_V + threadIdx.x; j < j1; j += REPORT_BLOCK) {
         const int64_t i0 = j * REPORT_V;
         int8_t qv[REPORT_V];
         float rv[REPORT_V];

@@ -45,7 +45,13 @@ constexpr int Q_SLOTS_CHUNK = 9;     // 9 x 16 bytes per thread
 constexpr int Q_BLOCK_LAYER = 512;   // fp32: 16384 elements per tile (64 KiB)
 constexpr int Q_BLOCK_CHUNK = 1024;  // fp32: 36864 elements per tile (144 KiB)
 constexpr int R_BLOCK = 512;
-constexpr int R_SLOTS = 1;           // 16 codes = 16 sums per thread (8192 per tile)
+// Reduce tiles hold 16 codes (16 sums) per thread and slot.  Wide tiles (two
+// slots, 16384 elements) halve the tiles and unit exchanges where most
+// elements sit in units wider than a narrow tile; narrow tiles (one slot,
+// 8192 elements) serve tables of short units, which would otherwise leave
+// most of a wide tile's lanes idle.
+constexpr int R_SLOTS_NARROW = 1;
+constexpr int R_SLOTS_WIDE = 2;
 
 // Units whose 16-byte slots span at most 64 * SMALL_SLOTS[table] slots are
 // "small": one wave handles a whole unit, in a first phase of the

@@ -804,8 +804,10 @@ __device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float 
     }
 }
 
-// Rank-order dequant-accumulate of the S slots of tile t into acc.
-template <int S, int BLOCK, int RG = 4>
+// Rank-order dequant-accumulate of the S slots of tile t into acc.  With
+// OFF32, a lane's loads are addressed from the tile's first slot by a 32-bit
+// offset (a tile spans at most S * BLOCK slots), which saves registers.
+template <int S, int BLOCK, int RG = 4, bool OFF32 = false>
 __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float (&acc)[S][RV]) {
     const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
@@ -828,11 +830,25 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             if (w0 + r >= a.W) break;
-            const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]);
+            if constexpr (OFF32) {
+                // slot jb + o, o = min(lane's slot - jb, jmax - jb): the same
+                // clamped slot as below (jb = min(j0, jmax))
+                const int64_t jb = j0 < jmax ? j0 : jmax;
+                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]) + jb;
+                const uint32_t lim = static_cast<uint32_t>(jmax - jb);
+                const uint32_t o0 = static_cast<uint32_t>(j0 - jb) + static_cast<uint32_t>(tid);
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-                v[r][s] = qv[j < jmax ? j : jmax];
+                for (int s = 0; s < S; ++s) {
+                    const uint32_t o = o0 + static_cast<uint32_t>(s * BLOCK);
+                    v[r][s] = qv[o < lim ? o : lim];
+                }
+            } else {
+                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+                    v[r][s] = qv[j < jmax ? j : jmax];
+                }
             }
         }
     };
@@ -1031,6 +1047,107 @@ void k_reduce_coop(const RArgs a) {
     launch_exit(a.ctl);
 }
 
+// Hot path for wide tiles (two slots per lane): as k_reduce_coop, but the
+// held tile's sums wait in LDS while the next tile is summed in registers.
+// Each lane parks its own sums (as 16-byte words, lane-contiguous, so the
+// stores and loads are free of bank conflicts) and reads back only its own,
+// so parking needs no barrier.  Two tiles of sums would not fit in
+// registers next to a tile's loads; in LDS they take 64 KiB per work group.
+template <int S, int BLOCK>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void k_reduce_coop_wide(const RArgs a) {
+    small_phase<BLOCK>(a.n_small, [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R>(a, item); });
+    __shared__ uint32_t sh[BLOCK / 64];
+    __shared__ uint32_t s_val[2];  // unit max, next ticket
+    __shared__ float4 park[S * RV / 4][BLOCK];
+    const int64_t total = a.n_tiles;
+    const uint32_t tag = launch_tag(a.ctl);
+    const int lane = threadIdx.x;
+    auto put = [&](const float (&acc)[S][RV]) {
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int g = 0; g < RV / 4; ++g)
+                park[s * (RV / 4) + g][lane] = make_float4(acc[s][4 * g], acc[s][4 * g + 1],
+                                                           acc[s][4 * g + 2], acc[s][4 * g + 3]);
+    };
+    auto get = [&](float (&acc)[S][RV]) {
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int g = 0; g < RV / 4; ++g) {
+                const float4 v = park[s * (RV / 4) + g][lane];
+                acc[s][4 * g] = v.x;
+                acc[s][4 * g + 1] = v.y;
+                acc[s][4 * g + 2] = v.z;
+                acc[s][4 * g + 3] = v.w;
+            }
+    };
+    if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+    __syncthreads();
+    int64_t tk = s_val[1];
+    Tile tc{};
+    uint32_t mc = 0;
+    uint64_t arr_c = 0;
+    if (tk < total) {
+        float acc[S][RV];
+        tc = load_desc(a.tiles, tk);
+        reduce_tile<S, BLOCK, 1, true>(a, tc, acc);
+        if (a.r) store_sum<S, BLOCK>(tc, acc, a.r);
+        mc = block_max<BLOCK>(acc_absmax<S>(acc), sh);
+        if (tc.count > 1 && threadIdx.x < 64)
+            arr_c = unit_publish(a.pub, a.cnt + tc.slot, static_cast<int32_t>(tk), mc, tag);
+        put(acc);
+    }
+    while (tk < total) {
+        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+        __syncthreads();
+        const int64_t tn = s_val[1];
+        const bool more = tn < total;
+        Tile tnx{};
+        uint32_t mn = 0;
+        uint64_t arr_n = 0;
+        float acc_n[S][RV];
+        if (more) {
+            tnx = load_desc(a.tiles, tn);
+            reduce_tile<S, BLOCK, 1, true>(a, tnx, acc_n);
+            if (a.r) store_sum<S, BLOCK>(tnx, acc_n, a.r);
+            mn = block_max<BLOCK>(acc_absmax<S>(acc_n), sh);
+            if (tnx.count > 1 && threadIdx.x < 64) {
+                arr_n = unit_publish(a.pub, a.cnt + tnx.slot, static_cast<int32_t>(tn), mn, tag);
+                if (__shfl(arr_n, 0, 64) % static_cast<uint64_t>(tnx.count) == 0)  // last: gather now
+                    (void)unit_max(a.pub, a.res + tnx.slot, static_cast<int32_t>(tn), tnx.first,
+                                   tnx.count, mn, arr_n, tag, a.faults);
+            }
+        }
+        uint32_t m = mc;
+        if (tc.count > 1) {
+            if (threadIdx.x < 64) {
+                const uint32_t um = unit_max(a.pub, a.res + tc.slot, static_cast<int32_t>(tk),
+                                             tc.first, tc.count, mc, arr_c, tag, a.faults);
+                if (threadIdx.x == 0) s_val[0] = um;
+            }
+            __syncthreads();
+            m = s_val[0];
+        }
+        const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+        if (threadIdx.x == 0 && tk == tc.first) a.scale_out[tc.unit] = sc;
+        {
+            float acc_c[S][RV];
+            get(acc_c);
+            requantize_tile<S, BLOCK>(tc, acc_c, quant_params(sc, true), a.q_out);
+        }
+        __syncthreads();
+        if (!more) break;
+        put(acc_n);
+        tc = tnx;
+        mc = mn;
+        arr_c = arr_n;
+        tk = tn;
+    }
+    launch_exit(a.ctl);
+}
+
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
 
 // Non-persistent reduce: the plain sum (R_SUM), and the two-launch form
@@ -1044,7 +1161,8 @@ __global__ __launch_bounds__(BLOCK) void k_reduce(const RArgs a) {
     const int32_t tix = (MODE == R_PASS1) ? a.list[blockIdx.x] : static_cast<int32_t>(blockIdx.x);
     const Tile t = load_desc(a.tiles, tix);
     float acc[S][RV];
-    reduce_tile<S, BLOCK>(a, t, acc);
+    if constexpr (S == 1) reduce_tile<S, BLOCK>(a, t, acc);
+    else reduce_tile<S, BLOCK, 1, true>(a, t, acc);
     if (a.r != nullptr && (MODE != R_FUSED || t.count == 1)) store_sum<S, BLOCK>(t, acc, a.r);
     if (MODE == R_SUM) return;
     uint32_t m;
@@ -1209,25 +1327,22 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
     return mul ? quantize_typed<__half, true>(a, t, s) : quantize_typed<__half, false>(a, t, s);
 }
 
-hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,
-                         hipStream_t s) {
-    if (!table_ready(t, 1)) return hipErrorInvalidValue;
-    RArgs a = a0;
-    a.tiles = t.d_tiles;
-    a.partial = t.d_partial;
-    a.n_tiles = t.n_tiles;
-    a.pub = t.d_pub;
-    a.res = t.d_res;
-    a.cnt = t.d_cnt;
-    a.ctl = t.d_ctl;
+template <int S>
+constexpr auto coop_reduce_kernel() {
+    if constexpr (S == R_SLOTS_WIDE) return k_reduce_coop_wide<S, R_BLOCK>;
+    else return k_reduce_coop<S, R_BLOCK>;
+}
+
+template <int S>
+hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free, hipStream_t s) {
     const dim3 block(R_BLOCK);
     if (!requantize) {
         a.list = nullptr;
-        hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
+        hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
                            block, 0, s, a);
         return hipGetLastError();
     }
-    constexpr auto coop = k_reduce_coop<R_SLOTS, R_BLOCK>;
+    constexpr auto coop = coop_reduce_kernel<S>();
     const int64_t resident = resident_groups<coop>(R_BLOCK);
     if (!wait_free && resident >= t.big_max_count) {
         RArgs c = a;
@@ -1242,13 +1357,30 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool 
     if (t.n_multi > 0) {
         RArgs p = a;
         p.list = t.d_multi;
-        hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_PASS1>),
-                           dim3(static_cast<unsigned>(t.n_multi)), block, 0, s, p);
+        hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_PASS1>), dim3(static_cast<unsigned>(t.n_multi)),
+                           block, 0, s, p);
     }
     a.list = nullptr;
-    hipLaunchKernelGGL((k_reduce<R_SLOTS, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
+    hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
                        block, 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,
+                         hipStream_t s) {
+    if (!table_ready(t, 1)) return hipErrorInvalidValue;
+    if (t.block != R_BLOCK || (t.slots != R_SLOTS_NARROW && t.slots != R_SLOTS_WIDE))
+        return hipErrorInvalidValue;
+    RArgs a = a0;
+    a.tiles = t.d_tiles;
+    a.partial = t.d_partial;
+    a.n_tiles = t.n_tiles;
+    a.pub = t.d_pub;
+    a.res = t.d_res;
+    a.cnt = t.d_cnt;
+    a.ctl = t.d_ctl;
+    if (t.slots == R_SLOTS_WIDE) return reduce_geom<R_SLOTS_WIDE>(a, t, requantize, wait_free, s);
+    return reduce_geom<R_SLOTS_NARROW>(a, t, requantize, wait_free, s);
 }
 
 }  // namespace gq

@@ -22,7 +22,7 @@ GQ_MAX_RANKS = 64
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
-           "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_faults",
+           "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_reduce_tile", "gq_units_faults",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
@@ -60,6 +60,8 @@ def _load():
     L.gq_units_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.gq_units_schedule.restype = st
     L.gq_units_schedule.argtypes = [vp, i32, ctypes.POINTER(i32)]
+    L.gq_units_reduce_tile.restype = st
+    L.gq_units_reduce_tile.argtypes = [vp, ctypes.POINTER(i64)]
     L.gq_units_faults.restype = st
     L.gq_units_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
     L.gq_absmax.restype = st
@@ -208,6 +210,14 @@ def gq_units_schedule(units, dtype_code=GQ_F32):
     for this table and element type."""
     v = ctypes.c_int32(-1)
     _check(lib.gq_units_schedule(units.handle, dtype_code, ctypes.byref(v)))
+    return v.value
+
+
+def gq_units_reduce_tile(units):
+    """Elements per work-group tile of the table's reduce (8192 or 16384),
+    chosen when the table was created."""
+    v = ctypes.c_int64(0)
+    _check(lib.gq_units_reduce_tile(units.handle, ctypes.byref(v)))
     return v.value
 
 

@@ -147,6 +147,15 @@ gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
 gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 
 /*
+ * gq_units_reduce_tile -- elements per work-group tile of a table's reduce:
+ * 16384 (wide tiles, when most elements sit in units wider than 8192
+ * elements: per-layer and per-chunk scales) or 8192 (narrow tiles, for
+ * tables of short units).  Chosen when the table is created; results do
+ * not depend on it.  elems: host pointer receiving the number.
+ */
+gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems);
+
+/*
  * gq_units_faults -- number of bounded waits that gave up since the table
  * was created.  The persistent kernels size their grid to what the device
  * keeps resident; a wait can only give up (after about a second) if the

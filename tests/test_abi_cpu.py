@@ -125,6 +125,11 @@ def test_argument_errors_before_any_device_call(gq):
     assert L.gq_reduce_requantize(q, s, 4, null, null, good, good, null) == gq.GQ_ERR_INVALID
     assert L.gq_reduce_requantize(q, s, 4, null, good + 4, good, good, null) == gq.GQ_ERR_ALIGN
     assert L.gq_reduce_requantize(q, s, 0, null, null, good, good, null) == gq.GQ_ERR_INVALID
+    # table queries
+    v32, v64 = ctypes.c_int32(0), ctypes.c_int64(0)
+    assert L.gq_units_schedule(null, gq.GQ_F32, ctypes.byref(v32)) == gq.GQ_ERR_INVALID
+    assert L.gq_units_reduce_tile(null, ctypes.byref(v64)) == gq.GQ_ERR_INVALID
+    assert "unit table" in gq.gq_last_error()
 
 
 def test_units_create_rejects_bad_tables(gq):

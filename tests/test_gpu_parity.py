@@ -313,7 +313,27 @@ def test_units_on_tile_boundaries(gq, oracle, kind):
     n = int(off[-1])
     xs = [_grad(rng, n, kind) for _ in range(3)]
     in_mul = 2.0 ** -16 if kind == F16 else 1.0
-    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "tile_bounds_k%d" % kind)
+    step = _run_and_compare(gq, oracle, xs, kind, off, in_mul, "tile_bounds_k%d" % kind)
+    assert gq.gq_units_reduce_tile(step.units) == 16384
+
+
+@pytest.mark.parametrize("W", [3, 8])
+def test_narrow_reduce_tiles(gq, oracle, W):
+    """A table of short units (most between 2049 and 8192 elements) takes
+    narrow reduce tiles of 8192 elements; units of one, two and three narrow
+    tiles and one element more and less sit among them."""
+    rng = np.random.default_rng(81 + W)
+    lens = [int(v) for v in rng.integers(2049, 8193, 150)]
+    for m in (1, 2, 3):
+        lens += [8192 * m - 1, 8192 * m, 8192 * m + 1]
+    lens += [1, 17, 2048, 300]
+    rng.shuffle(lens)
+    lens = [5] + lens
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, F32) for _ in range(W)]
+    step = _run_and_compare(gq, oracle, xs, F32, off, 1.0, "narrow_W%d" % W)
+    assert gq.gq_units_reduce_tile(step.units) == 8192
 
 
 def test_fp16_sixty_four_ranks(gq, oracle):

@@ -50,6 +50,8 @@ def test_workload_every_element(gq, oracle, cfg):
     want = oracle.allreduce_step(xs, _kind(w), off, w.in_mul)
     dx = [to_device(x) for x in xs]
     step = GpuStep(gq, off, w.W, _kind(w), w.n)
+    # per-layer units take wide reduce tiles, the small-tensor set narrow ones
+    assert gq.gq_units_reduce_tile(step.units) == (8192 if cfg == 5 else 16384)
     step.quantize(dx, w.in_mul)
     step.reduce(fused=True, with_r=False)
     compare_step(step.host(), want, w.W, check_r=False, label=w.name + "/bench")
