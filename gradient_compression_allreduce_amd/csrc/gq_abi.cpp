@@ -258,15 +258,20 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             t.slots = (2 * in_wide >= in_big) ? gq::R_SLOTS_WIDE : gq::R_SLOTS_NARROW;
         } else {
             // chunk schedule when most elements of the non-small units sit
-            // in units of one chunk tile
+            // in units that fill one chunk tile but not one layer tile (a
+            // shorter unit would leave most of a chunk tile's lanes idle),
+            // or when small units hold most elements (their per-wave phase
+            // runs faster in the chunk kernel); the layer schedule otherwise
             const int64_t cap = static_cast<int64_t>(gq::Q_BLOCK_CHUNK) * gq::Q_SLOTS_CHUNK;
-            int64_t in_single = 0, in_big = 0;
+            const int64_t layer_cap = static_cast<int64_t>(gq::Q_BLOCK_LAYER) * gq::Q_SLOTS_LAYER;
+            int64_t in_chunk = 0, in_big = 0;
             for (int64_t u = 0; u < n_units; ++u) {
                 if (span(u) <= small_cap) continue;
                 in_big += off[u + 1] - off[u];
-                if (span(u) <= cap) in_single += off[u + 1] - off[u];
+                if (span(u) > layer_cap && span(u) <= cap) in_chunk += off[u + 1] - off[u];
             }
-            t.sched = (2 * in_single >= in_big) ? gq::SCHED_CHUNK : gq::SCHED_LAYER;
+            const bool mostly_small = 2 * in_big < off[n_units] - off[0];
+            t.sched = (mostly_small || 2 * in_chunk >= in_big) ? gq::SCHED_CHUNK : gq::SCHED_LAYER;
             t.block = t.sched == gq::SCHED_CHUNK ? gq::Q_BLOCK_CHUNK : gq::Q_BLOCK_LAYER;
             t.slots = t.sched == gq::SCHED_CHUNK ? gq::Q_SLOTS_CHUNK : gq::Q_SLOTS_LAYER;
         }

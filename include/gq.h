@@ -136,11 +136,13 @@ gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
 
 /*
  * gq_units_schedule -- which schedule the fused quantize of a table uses for
- * elements of type dt: GQ_SCHED_LAYER (units spanning many work-group
- * tiles: per-tensor or per-layer scales) or GQ_SCHED_CHUNK (most elements
- * in units of at most one 144 KiB tile, which holds a 128 KiB chunk of
- * every tensor of 1 MiB or more: per-chunk scales, small tensors).
- * Chosen when the table is created; results do not depend on it.
+ * elements of type dt.  GQ_SCHED_CHUNK (144 KiB tiles, which hold a 128 KiB
+ * chunk of every tensor of 1 MiB or more) when most elements of the
+ * non-small units sit in units that fit one such tile but not one 64 KiB
+ * tile (per-chunk scales), or when small units (one wave's share) hold most
+ * elements; GQ_SCHED_LAYER (64 KiB tiles) otherwise: per-tensor or
+ * per-layer scales, and units too short to fill a 144 KiB tile.  Chosen
+ * when the table is created; results do not depend on it.
  */
 #define GQ_SCHED_LAYER 0
 #define GQ_SCHED_CHUNK 1

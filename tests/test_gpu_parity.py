@@ -225,6 +225,33 @@ def test_both_quantize_schedules(gq, oracle, kind):
     _run_and_compare(gq, oracle, xs, kind, tensor_off, in_mul, "layer_sched_k%d" % kind)
 
 
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+def test_mid_size_units_take_the_layer_schedule(gq, oracle, kind):
+    """Units longer than one wave's share but shorter than a layer tile (a
+    chunk tile would leave most of its lanes idle) take the layer schedule,
+    one tile each, and match the oracle; so do the same units with a few
+    chunk-sized ones among them."""
+    rng = np.random.default_rng(91 + kind)
+    esz = 4 if kind == F32 else 2
+    lo, hi = (4200, 16000) if kind == F32 else (8400, 32000)
+    lens = [int(v) for v in rng.integers(lo, hi, 120)]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(3)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    step = _run_and_compare(gq, oracle, xs, kind, off, in_mul, "mid_units_k%d" % kind,
+                            modes=("fused",))
+    assert gq.gq_units_schedule(step.units, kind) == gq.GQ_SCHED_LAYER
+    chunk = 131072 // esz
+    lens2 = lens[:100] + [chunk] * 40
+    off2 = np.concatenate([[0], np.cumsum(lens2)]).astype(np.int64)
+    n2 = int(off2[-1])
+    xs2 = [_grad(rng, n2, kind) for _ in range(3)]
+    step2 = _run_and_compare(gq, oracle, xs2, kind, off2, in_mul, "mid_chunk_k%d" % kind,
+                             modes=("fused",))
+    assert gq.gq_units_schedule(step2.units, kind) == gq.GQ_SCHED_CHUNK
+
+
 def test_errors_on_device(gq):
     """Argument errors reported by the ABI leave outputs untouched."""
     import torch

@@ -50,8 +50,11 @@ def test_workload_every_element(gq, oracle, cfg):
     want = oracle.allreduce_step(xs, _kind(w), off, w.in_mul)
     dx = [to_device(x) for x in xs]
     step = GpuStep(gq, off, w.W, _kind(w), w.n)
-    # per-layer units take wide reduce tiles, the small-tensor set narrow ones
+    # per-layer units take wide reduce tiles, the small-tensor set narrow ones;
+    # the small-tensor set takes the chunk schedule, whole tensors the layer one
     assert gq.gq_units_reduce_tile(step.units) == (8192 if cfg == 5 else 16384)
+    assert gq.gq_units_schedule(step.units, _kind(w)) == (
+        gq.GQ_SCHED_CHUNK if cfg == 5 else gq.GQ_SCHED_LAYER)
     step.quantize(dx, w.in_mul)
     step.reduce(fused=True, with_r=False)
     compare_step(step.host(), want, w.W, check_r=False, label=w.name + "/bench")
