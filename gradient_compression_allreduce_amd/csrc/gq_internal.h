@@ -30,9 +30,10 @@ enum TableId { TAB_Q32 = 0, TAB_Q16 = 1, TAB_R = 2, TAB_COUNT = 3 };
 
 // Schedules of the persistent quantize kernel, chosen per unit table:
 //  SCHED_LAYER  units spanning many tiles (per-tensor or per-layer scales):
-//               512-thread tiles; a tile's max is published one tile ahead
-//               of the wait for its unit max, which leaves slack for the
-//               unit's other tiles to arrive.
+//               512-thread tiles; a work group holds two published tiles
+//               (one parked in LDS), so a tile's unit max is first asked for
+//               two tiles after its own max was published, and the older
+//               tile is coded while the next tile's loads are in flight.
 //  SCHED_CHUNK  units of about one tile (per-chunk scales, small tensors):
 //               1024-thread tiles of 144 KiB, which hold a whole chunk of
 //               the chunk plan for every tensor of 1 MiB or more (those

@@ -372,6 +372,40 @@ __device__ __forceinline__ int code_of(float g, const QuantParams &p) {
     else return 0;
 }
 
+// Codes of one slot j of tile t (V elements held raw), for one code mode.
+template <typename TIn, bool MUL, int MODE>
+__device__ __forceinline__ void quantize_slot(const typename In<TIn>::Raw &raw, int64_t j,
+                                              const Tile &t, float in_mul, const QuantParams &p,
+                                              int8_t *q) {
+    constexpr int V = In<TIn>::V;
+    float g[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        g[k] = In<TIn>::elem(raw, k);
+        if (MUL) g[k] = __fmul_rn(g[k], in_mul);
+    }
+    uint32_t pk[V / 4];
+#pragma unroll
+    for (int k = 0; k < V / 4; ++k) {
+        if constexpr (MODE == CM_FAST) {
+            pk[k] = codes4_fast(g[4 * k], g[4 * k + 1], g[4 * k + 2], g[4 * k + 3], p.s, p.r);
+        } else {
+            pk[k] = pack4(code_of<MODE>(g[4 * k], p), code_of<MODE>(g[4 * k + 1], p),
+                          code_of<MODE>(g[4 * k + 2], p), code_of<MODE>(g[4 * k + 3], p));
+        }
+    }
+    const int64_t i0 = j * V;
+    if constexpr (V == 4) {
+        const uint32_t p0 = pk[0];
+        if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint32_t *>(q + i0) = p0;
+        else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, 0, 0, 0));
+    } else {
+        const uint32_t p0 = pk[0], p1 = pk[1];
+        if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint2 *>(q + i0) = make_uint2(p0, p1);
+        else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, p1, 0, 0));
+    }
+}
+
 // Codes of the S held slots of tile t, for one code mode.
 template <typename TIn, int S, int BLOCK, bool MUL, int MODE>
 __device__ __forceinline__ void quantize_tile_mode(const typename In<TIn>::Raw (&raw)[S],
@@ -384,32 +418,25 @@ __device__ __forceinline__ void quantize_tile_mode(const typename In<TIn>::Raw (
     for (int s = 0; s < S; ++s) {
         const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
         if (j >= j1) continue;
-        float g[V];
+        quantize_slot<TIn, MUL, MODE>(raw[s], j, t, in_mul, p, q);
+    }
+}
+
+// The same for a tile parked in LDS (slot s of lane l at park[s][l]); each
+// lane reads back only what it parked.
+template <typename TIn, int S, int BLOCK, bool MUL, int MODE>
+__device__ __forceinline__ void quantize_parked_mode(const typename In<TIn>::Raw (*park)[BLOCK],
+                                                     const Tile &t, float in_mul,
+                                                     const QuantParams &p, int8_t *q) {
+    constexpr int V = In<TIn>::V;
+    const int64_t tid = opaque_tid<BLOCK>();
+    const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            g[k] = In<TIn>::elem(raw[s], k);
-            if (MUL) g[k] = __fmul_rn(g[k], in_mul);
-        }
-        uint32_t pk[V / 4];
-#pragma unroll
-        for (int k = 0; k < V / 4; ++k) {
-            if constexpr (MODE == CM_FAST) {
-                pk[k] = codes4_fast(g[4 * k], g[4 * k + 1], g[4 * k + 2], g[4 * k + 3], p.s, p.r);
-            } else {
-                pk[k] = pack4(code_of<MODE>(g[4 * k], p), code_of<MODE>(g[4 * k + 1], p),
-                              code_of<MODE>(g[4 * k + 2], p), code_of<MODE>(g[4 * k + 3], p));
-            }
-        }
-        const int64_t i0 = j * V;
-        if constexpr (V == 4) {
-            const uint32_t p0 = pk[0];
-            if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint32_t *>(q + i0) = p0;
-            else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, 0, 0, 0));
-        } else {
-            const uint32_t p0 = pk[0], p1 = pk[1];
-            if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint2 *>(q + i0) = make_uint2(p0, p1);
-            else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, p1, 0, 0));
-        }
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        if (j >= j1) continue;
+        const typename In<TIn>::Raw r = park[s][threadIdx.x];
+        quantize_slot<TIn, MUL, MODE>(r, j, t, in_mul, p, q);
     }
 }
 
@@ -647,10 +674,16 @@ void k_quantize_chunk(const QArgs a) {
 }
 
 // Hot path, SCHED_LAYER: every tile of every rank, one read of the input.
-// A work group loads its next tile and publishes that tile's max before it
-// waits for the current tile's unit max, so it never blocks while holding an
-// unpublished tile (see the scheduling note above), and a tile's max is
-// published a whole tile ahead of the wait for its unit.
+// A work group holds up to two published tiles whose unit max it may still
+// need: C in registers and P, the older one, parked in LDS (64 KiB).  Per
+// ticket it: takes the ticket (and polls P's unit result word once, in the
+// same round trip); issues the new tile N's loads; codes P from LDS while
+// they fly if P's unit max is known; takes N's max and publishes it; only
+// then, if P is still open, waits for P's unit max and codes P; parks C in
+// LDS as the next P and keeps N in registers as the next C.  A tile's unit
+// max is thus first asked for two tiles after the tile was published, when
+// it is usually known, and the work group blocks only with every tile it
+// holds published (see the scheduling note above).
 template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_layer(const QArgs a) {
@@ -659,68 +692,152 @@ void k_quantize_layer(const QArgs a) {
         quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
     });
     __shared__ uint32_t sh[BLOCK / 64];
-    __shared__ uint32_t s_val[2];  // unit max, next ticket
+    __shared__ uint32_t s_val[3];  // unit max, ticket, polled-ready flag
+    __shared__ Raw park[S][BLOCK];
     const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
     const uint32_t tag = launch_tag(a.ctl);
-    if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
-    __syncthreads();
-    int64_t tk = s_val[1];
-    Raw cur[S], nxt[S];
-    Tile tc{};
-    int wc = 0;
-    uint32_t mc = 0;          // cur's own max
-    uint64_t arr_c = 0;       // cur's arrival count (lane 0 of wave 0)
-    // load a tile, take its max and publish it (wave 0 gathers at once if it
-    // was the unit's last arrival)
-    auto start_tile = [&](int64_t t_k, Raw (&buf)[S], Tile &t, int &w, uint32_t &m, uint64_t &arr) {
-        w = static_cast<int>(t_k / a.n_tiles);
+    const int lane = threadIdx.x;
+    // held tiles C (slots in A) and P (slots parked): ticket, rank,
+    // descriptor, max (the unit max once known) and arrival count
+    Raw A[S], B[S];
+    bool has_c = false, known_c = false, has_p = false, known_p = false;
+    Tile tc{}, tp{};
+    int wc = 0, wp = 0;
+    int64_t kc = 0, kp = 0;
+    uint32_t mc = 0, mp = 0;
+    uint64_t arr_c = 0, arr_p = 0;
+    // max of a loaded tile, its publication, and the gather if it was its
+    // unit's last arrival; returns whether m is the unit max
+    auto finish_tile = [&](int64_t t_k, Raw (&buf)[S], const Tile &t, int w, uint32_t &m,
+                           uint64_t &arr) -> bool {
         const int32_t tix = static_cast<int32_t>(t_k - static_cast<int64_t>(w) * a.n_tiles);
-        t = load_desc(a.tiles, tix);
-        issue_tile<TIn, S, BLOCK>(a.x[w], t, a.n, buf);
         m = block_max<BLOCK>(fix_tile<TIn, S, BLOCK>(a.x[w], t, a.n, buf), sh);
-        if (t.count > 1 && threadIdx.x < 64) {
+        if (t.count == 1) return true;
+        if (threadIdx.x < 64) {
             uint64_t *pub = a.pub + static_cast<int64_t>(w) * a.n_tiles;
             const int64_t u = static_cast<int64_t>(w) * a.n_multi_units + t.slot;
             arr = unit_publish(pub, a.cnt + u, tix, m, tag);
-            if (__shfl(arr, 0, 64) % static_cast<uint64_t>(t.count) == 0)
-                (void)unit_max(pub, a.res + u, tix, t.first, t.count, m, arr, tag, a.faults);
+            uint32_t last = 0;
+            if (__shfl(arr, 0, 64) % static_cast<uint64_t>(t.count) == 0) {
+                const uint32_t um = unit_max(pub, a.res + u, tix, t.first, t.count, m, arr, tag,
+                                             a.faults);
+                last = 1;
+                if (threadIdx.x == 0) s_val[0] = um;
+            }
+            if (threadIdx.x == 0) s_val[2] = last;
         }
-    };
-    if (tk < total) start_tile(tk, cur, tc, wc, mc, arr_c);
-    while (tk < total) {
-        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
         __syncthreads();
-        const int64_t tn = s_val[1];
+        const bool known = s_val[2] != 0;
+        if (known) m = s_val[0];
+        __syncthreads();
+        return known;
+    };
+    auto code_parked = [&]() {
+        const int32_t tix = static_cast<int32_t>(kp - static_cast<int64_t>(wp) * a.n_tiles);
+        const float sc = __fdiv_rn(In<TIn>::max_value(mp, a.in_mul, MUL), 127.0f);
+        if (threadIdx.x == 0 && tix == tp.first) a.scale[wp][tp.unit] = sc;
+        const QuantParams qp = quant_params(sc, true);
+        const int mode = __builtin_amdgcn_readfirstlane(qp.mode);
+        if (mode == CM_FAST)
+            quantize_parked_mode<TIn, S, BLOCK, MUL, CM_FAST>(park, tp, a.in_mul, qp, a.q[wp]);
+        else if (mode == CM_EXACT)
+            quantize_parked_mode<TIn, S, BLOCK, MUL, CM_EXACT>(park, tp, a.in_mul, qp, a.q[wp]);
+        else
+            quantize_parked_mode<TIn, S, BLOCK, MUL, CM_ZERO>(park, tp, a.in_mul, qp, a.q[wp]);
+    };
+    bool tickets_left = true;
+    if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl);
+    __syncthreads();
+    {
+        const int64_t tk = s_val[1];
+        __syncthreads();
+        if (tk < total) {
+            wc = static_cast<int>(tk / a.n_tiles);
+            tc = load_desc(a.tiles, static_cast<int32_t>(tk - static_cast<int64_t>(wc) * a.n_tiles));
+            issue_tile<TIn, S, BLOCK>(a.x[wc], tc, a.n, A);
+            known_c = finish_tile(tk, A, tc, wc, mc, arr_c);
+            kc = tk;
+            has_c = true;
+        } else {
+            tickets_left = false;
+        }
+    }
+    while (has_c || has_p) {
+        // one round trip: the next ticket, and one look at P's result word
+        const int64_t up = static_cast<int64_t>(wp) * a.n_multi_units + tp.slot;
+        if (threadIdx.x == 0) {
+            if (tickets_left) s_val[1] = take_ticket(a.ctl);
+            uint32_t ready = 0;
+            if (has_p && !known_p) {
+                const uint64_t v = __hip_atomic_load(a.res + up, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if (static_cast<uint32_t>(v >> 32) == tag) {
+                    ready = 1;
+                    s_val[0] = static_cast<uint32_t>(v);
+                }
+            }
+            s_val[2] = ready;
+        }
+        __syncthreads();
+        const int64_t tn = tickets_left ? static_cast<int64_t>(s_val[1]) : total;
+        if (has_p && !known_p && s_val[2] != 0) {
+            known_p = true;
+            mp = s_val[0];
+        }
+        __syncthreads();
         const bool more = tn < total;
+        if (!more) tickets_left = false;
         Tile tnx{};
         int wn = 0;
+        if (more) {
+            wn = static_cast<int>(tn / a.n_tiles);
+            tnx = load_desc(a.tiles, static_cast<int32_t>(tn - static_cast<int64_t>(wn) * a.n_tiles));
+            issue_tile<TIn, S, BLOCK>(a.x[wn], tnx, a.n, B);
+        }
+        if (has_p && known_p) {  // while N's loads fly
+            code_parked();
+            has_p = false;
+        }
         uint32_t mn = 0;
         uint64_t arr_n = 0;
-        if (more) start_tile(tn, nxt, tnx, wn, mn, arr_n);
-        const int32_t tix = static_cast<int32_t>(tk - static_cast<int64_t>(wc) * a.n_tiles);
-        uint32_t m = mc;
-        if (tc.count > 1) {
+        bool known_n = false;
+        if (more) known_n = finish_tile(tn, B, tnx, wn, mn, arr_n);
+        if (has_p) {  // every held tile is published: safe to wait
             if (threadIdx.x < 64) {
-                const int64_t u = static_cast<int64_t>(wc) * a.n_multi_units + tc.slot;
-                const uint32_t um = unit_max(a.pub + static_cast<int64_t>(wc) * a.n_tiles, a.res + u,
-                                             tix, tc.first, tc.count, mc, arr_c, tag, a.faults);
+                const int32_t tix = static_cast<int32_t>(kp - static_cast<int64_t>(wp) * a.n_tiles);
+                const uint32_t um = unit_max(a.pub + static_cast<int64_t>(wp) * a.n_tiles, a.res + up,
+                                             tix, tp.first, tp.count, mp, arr_p, tag, a.faults);
                 if (threadIdx.x == 0) s_val[0] = um;
             }
             __syncthreads();
-            m = s_val[0];
+            mp = s_val[0];
+            __syncthreads();
+            code_parked();
+            has_p = false;
         }
-        const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
-        if (threadIdx.x == 0 && tix == tc.first) a.scale[wc][tc.unit] = sc;
-        quantize_tile<TIn, S, BLOCK, MUL>(cur, tc, a.in_mul, quant_params(sc, true), a.q[wc]);
-        __syncthreads();
-        if (!more) break;
+        if (has_c) {  // C becomes P
 #pragma unroll
-        for (int s = 0; s < S; ++s) cur[s] = nxt[s];
-        tc = tnx;
-        wc = wn;
-        tk = tn;
-        mc = mn;
-        arr_c = arr_n;
+            for (int s = 0; s < S; ++s) park[s][lane] = A[s];
+            tp = tc;
+            wp = wc;
+            kp = kc;
+            mp = mc;
+            known_p = known_c;
+            arr_p = arr_c;
+            has_p = true;
+            has_c = false;
+        }
+        if (more) {  // N becomes C
+#pragma unroll
+            for (int s = 0; s < S; ++s) A[s] = B[s];
+            tc = tnx;
+            wc = wn;
+            kc = tn;
+            mc = mn;
+            known_c = known_n;
+            arr_c = arr_n;
+            has_c = true;
+        }
     }
     launch_exit(a.ctl);
 }
