@@ -200,6 +200,19 @@ def test_unit_larger_than_resident_groups(gq, oracle, kind):
                      modes=("fused",))
 
 
+def test_unit_of_exactly_the_resident_grid(gq, oracle):
+    """A unit of 512 layer tiles (and 512 wide reduce tiles): as many tiles
+    as 256 compute units keep resident work groups, the largest unit the
+    persistent kernels take, so every resident group holds one of its tiles
+    at once; small units around it."""
+    rng = np.random.default_rng(27)
+    lens = [300, 512 * 16384, 5000, 7]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, F32) for _ in range(2)]
+    _run_and_compare(gq, oracle, xs, F32, off, 1.0, "resident_grid_unit", modes=("fused",))
+
+
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
 def test_both_quantize_schedules(gq, oracle, kind):
     """The same data under a per-chunk unit table (chunk schedule) and a
