@@ -224,9 +224,10 @@ gq_status gq_requantize(const float *r, const gq_units *u, float *scale_out,
 
 /*
  * gq_reduce_requantize -- gq_reduce_dequant followed by gq_requantize,
- * fused: the sum stays on chip for units of up to as many 8192-element
- * tiles as the device keeps resident (it is recomputed from the codes in a
- * second pass for larger units).
+ * fused: the sum stays on chip for units of up to as many reduce tiles
+ * (gq_units_reduce_tile elements each) as the device keeps resident work
+ * groups (it is recomputed from the codes in a second pass for larger
+ * units).
  * Results are bit-identical to the two separate calls.
  * r_out      NULL, or a device array of n fp32 that also receives the sum.
  */
