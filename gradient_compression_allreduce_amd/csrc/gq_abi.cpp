@@ -240,7 +240,7 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
     for (int ti = 0; ti < gq::TAB_COUNT && e == hipSuccess; ++ti) {
         const int V = gq::kSlotElems[ti];
         gq::Table &t = U->tab[ti];
-        const int64_t small_cap =
+        int64_t small_cap =
             64 * static_cast<int64_t>(ti == gq::TAB_R ? gq::SMALL_SLOTS_R : gq::SMALL_SLOTS_Q);
         auto span = [&](int64_t u) { return (off[u + 1] + V - 1) / V - off[u] / V; };
         if (ti == gq::TAB_R) {
@@ -256,6 +256,9 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             t.sched = gq::SCHED_LAYER;
             t.block = gq::R_BLOCK;
             t.slots = (2 * in_wide >= in_big) ? gq::R_SLOTS_WIDE : gq::R_SLOTS_NARROW;
+            // the narrow kernel's waves also take units of up to twice their
+            // slots, in two halves
+            if (t.slots == gq::R_SLOTS_NARROW) small_cap *= 2;
         } else {
             // chunk schedule when most elements of the non-small units sit
             // in units that fill one chunk tile but not one layer tile (a

@@ -1077,11 +1077,62 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
     else requantize_tile_mode<S, BLOCK, CM_ZERO>(t, acc, p, q);
 }
 
-// Small units: one wave per unit.
-template <int SR>
-__device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item) {
+// Small units: one wave per unit.  With HALVES (narrow reduce tables), a
+// unit of up to twice the wave's 64 * SR slots is summed in two halves, the
+// first half's sums parked meanwhile in this wave's 8 KiB of LDS (slot
+// group g of lane l at wpark[g * 64 + l]; each lane reads back only its
+// own), and both halves are requantized with the whole unit's scale.
+template <int SR, bool HALVES>
+__device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, float4 *wpark) {
     const Tile t = load_desc(a.small, item);
     float acc[SR][RV];
+    const int64_t half_end = (t.begin / RV + 64 * SR) * RV;
+    if (HALVES && t.end > half_end) {
+        const int lane = threadIdx.x & 63;
+        uint32_t m = 0;
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            Tile th = t;
+            if (h == 0) th.end = half_end;
+            else th.begin = half_end;
+            reduce_tile<SR, 64, 1>(a, th, acc);
+            if (a.r) store_sum<SR, 64>(th, acc, a.r);
+            m = umax(m, acc_absmax<SR>(acc));
+            if (h == 0) {
+#pragma unroll
+                for (int s = 0; s < SR; ++s)
+#pragma unroll
+                    for (int g = 0; g < RV / 4; ++g)
+                        wpark[(s * (RV / 4) + g) * 64 + lane] = make_float4(
+                            acc[s][4 * g], acc[s][4 * g + 1], acc[s][4 * g + 2], acc[s][4 * g + 3]);
+            }
+        }
+        m = wave_max(m);
+        const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+        if (lane == 0) a.scale_out[t.unit] = sc;
+        const QuantParams qp = quant_params(sc, true);
+#pragma unroll 1
+        for (int h = 1; h >= 0; --h) {  // the second half is still in registers
+            Tile th = t;
+            if (h == 0) {
+                th.end = half_end;
+#pragma unroll
+                for (int s = 0; s < SR; ++s)
+#pragma unroll
+                    for (int g = 0; g < RV / 4; ++g) {
+                        const float4 v = wpark[(s * (RV / 4) + g) * 64 + lane];
+                        acc[s][4 * g] = v.x;
+                        acc[s][4 * g + 1] = v.y;
+                        acc[s][4 * g + 2] = v.z;
+                        acc[s][4 * g + 3] = v.w;
+                    }
+            } else {
+                th.begin = half_end;
+            }
+            requantize_tile<SR, 64>(th, acc, qp, a.q_out);
+        }
+        return;
+    }
     reduce_tile<SR, 64, 1>(a, t, acc);
     if (a.r) store_sum<SR, 64>(t, acc, a.r);
     const uint32_t m = wave_max(acc_absmax<SR>(acc));
@@ -1097,7 +1148,11 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item) 
 template <int S, int BLOCK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_reduce_coop(const RArgs a) {
-    small_phase<BLOCK>(a.n_small, [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R>(a, item); });
+    // the small phase's half-unit sums: 8 KiB per wave
+    __shared__ float4 spark[(BLOCK / 64) * SMALL_SLOTS_R * (RV / 4) * 64];
+    float4 *wpark = spark + (threadIdx.x >> 6) * (SMALL_SLOTS_R * (RV / 4) * 64);
+    small_phase<BLOCK>(a.n_small,
+                       [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R, true>(a, item, wpark); });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
     const int64_t total = a.n_tiles;
@@ -1173,7 +1228,8 @@ void k_reduce_coop(const RArgs a) {
 template <int S, int BLOCK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_reduce_coop_wide(const RArgs a) {
-    small_phase<BLOCK>(a.n_small, [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R>(a, item); });
+    small_phase<BLOCK>(a.n_small,
+                       [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R, false>(a, item, nullptr); });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
     __shared__ float4 park[S * RV / 4][BLOCK];

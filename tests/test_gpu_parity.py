@@ -360,13 +360,15 @@ def test_units_on_tile_boundaries(gq, oracle, kind):
 @pytest.mark.parametrize("W", [3, 8])
 def test_narrow_reduce_tiles(gq, oracle, W):
     """A table of short units (most between 2049 and 8192 elements) takes
-    narrow reduce tiles of 8192 elements; units of one, two and three narrow
-    tiles and one element more and less sit among them."""
+    narrow reduce tiles of 8192 elements, and its waves take units of up to
+    4096 elements in two halves; units of one, two and three narrow tiles,
+    units at the one-wave and two-half limits, and one element more and
+    less sit among them."""
     rng = np.random.default_rng(81 + W)
     lens = [int(v) for v in rng.integers(2049, 8193, 150)]
     for m in (1, 2, 3):
         lens += [8192 * m - 1, 8192 * m, 8192 * m + 1]
-    lens += [1, 17, 2048, 300]
+    lens += [1, 17, 2048, 300, 2047, 2049, 2050, 4080, 4095, 4096, 4097, 4111, 4112, 4113]
     rng.shuffle(lens)
     lens = [5] + lens
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
