@@ -385,3 +385,47 @@ def test_fp16_sixty_four_ranks(gq, oracle):
     off = _offsets(rng, n, 500, 30_000)
     xs = [_grad(rng, n, F16) for _ in range(64)]
     _run_and_compare(gq, oracle, xs, F16, off, 2.0 ** -16, "f16_W64", modes=("fused",))
+
+
+def _random_table(rng, n_target):
+    """Unit lengths from one of several size regimes (tiny, small, mid-size,
+    layer-size, or log-uniform over all), optionally starting past 0."""
+    mode = int(rng.integers(0, 5))
+    lo_hi = [(1, 64), (1, 5000), (2000, 40000), (30000, 600000)]
+    lens, tot = [], 0
+    while tot < n_target:
+        L = int(rng.integers(*lo_hi[mode])) if mode < 4 else int(10 ** rng.uniform(0, 6))
+        lens.append(L)
+        tot += L
+    start = int(rng.integers(0, 40)) if rng.random() < 0.3 else 0
+    return np.concatenate([[start], start + np.cumsum(lens)]).astype(np.int64)
+
+
+def test_random_tables_sweep(gq, oracle):
+    """Seeded random unit tables, rank counts and element types through the
+    fused step (the benchmark's launch shape, with the sum kept): every case
+    bit-exact, and every pairing of quantize schedule and reduce tile width
+    reached."""
+    rng = np.random.default_rng(2024)
+    seen = set()
+    for c in range(120):
+        kind = F32 if rng.random() < 0.6 else F16
+        W = int(rng.choice([1, 2, 3, 5, 8, 16]))
+        off = _random_table(rng, int(10 ** rng.uniform(2, 6.3)))
+        n = int(off[-1])
+        xs = [_grad(rng, n, kind) for _ in range(W)]
+        in_mul = 2.0 ** -16 if kind == F16 else 1.0
+        step = GpuStep(gq, off, W, kind, n)
+        seen.add((gq.gq_units_schedule(step.units, kind), gq.gq_units_reduce_tile(step.units)))
+        say("sweep case", c, "kind", kind, "W", W, "n", n, "units", off.size - 1)
+        want = oracle.allreduce_step(xs, kind, off, in_mul)
+        step.quantize([to_device(x) for x in xs], in_mul)
+        step.reduce(fused=True, with_r=True)
+        got = step.host()
+        s0 = int(off[0])
+        if s0:
+            got = dict(got, q=[q[s0:] for q in got["q"]], r=got["r"][s0:], q_out=got["q_out"][s0:])
+            want = dict(want, q=[q[s0:] for q in want["q"]], r=want["r"][s0:],
+                        q_out=want["q_out"][s0:])
+        compare_step(got, want, W, check_r=True, label="sweep%d" % c)
+    assert len(seen) == 4, seen
