@@ -411,6 +411,8 @@ def main():
         sys.exit(3)
     sched = gq.gq_units_schedule(units, gq.GQ_F32 if kind == 0 else gq.GQ_F16)
     qkernel = "k_quantize_chunk" if sched == gq.GQ_SCHED_CHUNK else "k_quantize_layer"
+    rkernel = "k_reduce_coop_wide" if gq.gq_units_reduce_tile(units) == 16384 else "k_reduce_coop"
+    r_achieved = br / (r_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -447,6 +449,12 @@ def main():
                      "unit": "GB/s", "frac": round(q_achieved / (HBM_PEAK / 1e9), 4),
                      "traffic": measured_traffic(qkernel, w.name),
                      "algorithmic_bytes_per_launch": bq},
+        # the other stage's kernel, the same way
+        "roofline_reduce": {"bound": "hbm", "kernel": rkernel,
+                            "achieved": round(r_achieved, 1), "peak": HBM_PEAK / 1e9,
+                            "unit": "GB/s", "frac": round(r_achieved / (HBM_PEAK / 1e9), 4),
+                            "traffic": measured_traffic(rkernel, w.name),
+                            "algorithmic_bytes_per_launch": br},
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "kernel_source": kernel_source_hash(),
         "wall_s": round(wall, 3),
