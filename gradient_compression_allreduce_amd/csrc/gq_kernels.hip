@@ -48,11 +48,7 @@
 //     same integer as q0 and the division is skipped, otherwise it is done
 //     exactly;
 //   * the reduction adds fl(q_w * s_w) to a +0 accumulator in rank order
-//     with separate rounded multiplies and adds (never contracted).  The
-//     product is formed as fma(q_w + 128, s_w, -128 s_w), whose single
-//     rounding of the exact value (q_w + 128 - 128) s_w equals fl(q_w s_w)
-//     when 128 s_w does not overflow (|s_w| < 2^121); otherwise it is a
-//     plain multiply.
+//     with separate rounded multiplies and adds (never contracted).
 #include <hip/hip_fp16.h>
 
 #include "gq_internal.h"
@@ -902,21 +898,18 @@ __global__ __launch_bounds__(BLOCK) void k_quantize(const QArgs a) {
 
 constexpr int RV = 16;  // codes per reduce slot
 
-// acc += fl(q * sw) for the 16 codes of each held slot.  u = q + 128 is
-// taken from the byte with its top bit flipped (exact as a float).
-template <int S, bool VIA_FMA>
-__device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float neg128,
-                                           float (&acc)[S][RV]) {
+// acc += fl(q * sw) for the 16 codes of each held slot: each code is
+// converted from its signed byte (one instruction with a byte-select source
+// operand) and multiplied by sw with one rounding, then added.
+template <int S>
+__device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float (&acc)[S][RV]) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const uint32_t wd[4] = {v[s].x ^ 0x80808080u, v[s].y ^ 0x80808080u,
-                                v[s].z ^ 0x80808080u, v[s].w ^ 0x80808080u};
+        const uint32_t wd[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
         for (int k = 0; k < RV; ++k) {
-            const float u = static_cast<float>((wd[k >> 2] >> (8 * (k & 3))) & 0xffu);
-            const float d = VIA_FMA ? __builtin_fmaf(u, sw, neg128)
-                                    : __fmul_rn(__fsub_rn(u, 128.0f), sw);
-            acc[s][k] = __fadd_rn(acc[s][k], d);
+            const int c = static_cast<int8_t>((wd[k >> 2] >> (8 * (k & 3))) & 0xffu);
+            acc[s][k] = __fadd_rn(acc[s][k], __fmul_rn(static_cast<float>(c), sw));
         }
     }
 }
@@ -982,11 +975,7 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
                 if (!(j < j1 && j < nfull))
                     cur[r][s] = (j < j1) ? load_tail16(a.q[w], j * RV, a.n) : make_uint4(0, 0, 0, 0);
             }
-            const float sw = a.scale[w][t.unit];
-            const float neg128 = -128.0f * sw;
-            const bool via_fma = fabsf(sw) < 0x1p121f;  // false for inf and NaN too (uniform)
-            if (via_fma) accumulate<S, true>(cur[r], sw, neg128, acc);
-            else accumulate<S, false>(cur[r], sw, neg128, acc);
+            accumulate<S>(cur[r], a.scale[w][t.unit], acc);
         }
 #pragma unroll
         for (int r = 0; r < RG; ++r)
