@@ -4,10 +4,12 @@
 //
 // The work is bandwidth-bound streaming (no dense contraction, so no MFMA).
 // Kernels walk host-built "tiles" (contiguous element ranges of one unit);
-// one work group owns one tile of one rank at a time.  A tile is read with
+// a work group loads one tile of one rank at a time (and may hold one or
+// two earlier tiles whose unit max it still needs).  A tile is read with
 // 16-byte loads, one slot of V elements per lane per step, so a wave touches
-// 1 KiB of contiguous memory per load instruction, and the tile stays in
-// registers between the max and the code pass.
+// 1 KiB of contiguous memory per load instruction, and the tile stays on
+// chip (registers, or LDS while it waits for its unit max) between the max
+// and the code pass.
 //
 // The hot path is one persistent kernel per stage, launched with no more
 // work groups (G) than the device keeps resident at once.  Work groups take
@@ -1130,10 +1132,11 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
     requantize_tile<SR, 64>(t, acc, quant_params(sc, true), a.q_out);
 }
 
-// Hot path: reduce + requantize of every tile, one read of the codes.  A
-// work group sums its next tile (and publishes that tile's max) before it
-// waits for the current tile's unit max, so the wait overlaps a whole tile
-// of memory traffic.
+// Hot path for narrow tiles (one slot per lane): reduce + requantize of
+// every tile, one read of the codes.  A work group sums its next tile (and
+// publishes that tile's max) before it waits for the current tile's unit
+// max, so the wait overlaps a whole tile of memory traffic; both tiles'
+// sums are in registers.
 template <int S, int BLOCK>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_reduce_coop(const RArgs a) {
