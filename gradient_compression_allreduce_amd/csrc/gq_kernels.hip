@@ -1068,11 +1068,13 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
     else requantize_tile_mode<S, BLOCK, CM_ZERO>(t, acc, p, q);
 }
 
-// Small units: one wave per unit.  With HALVES (narrow reduce tables), a
-// unit of up to twice the wave's 64 * SR slots is summed in two halves, the
-// first half's sums parked meanwhile in this wave's 8 KiB of LDS (slot
-// group g of lane l at wpark[g * 64 + l]; each lane reads back only its
-// own), and both halves are requantized with the whole unit's scale.
+// Small units: one wave per unit.  A unit of at most 64 slots takes one
+// slot per lane and more ranks in flight.  With HALVES (narrow reduce
+// tables), a unit of up to twice the wave's 64 * SR slots is summed in two
+// halves, the first half's sums parked meanwhile in this wave's 8 KiB of
+// LDS (slot group g of lane l at wpark[g * 64 + l]; each lane reads back
+// only its own), and both halves are requantized with the whole unit's
+// scale.
 template <int SR, bool HALVES>
 __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, float4 *wpark) {
     const Tile t = load_desc(a.small, item);
@@ -1122,6 +1124,18 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
             }
             requantize_tile<SR, 64>(th, acc, qp, a.q_out);
         }
+        return;
+    }
+    if ((t.end + RV - 1) / RV - t.begin / RV <= 64) {
+        // one slot per lane: registers for the ranks' loads four at a time,
+        // eight in flight, instead of one or two
+        float acc1[1][RV];
+        reduce_tile<1, 64, 4>(a, t, acc1);
+        if (a.r) store_sum<1, 64>(t, acc1, a.r);
+        const uint32_t m = wave_max(acc_absmax<1>(acc1));
+        const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+        if ((threadIdx.x & 63) == 0) a.scale_out[t.unit] = sc;
+        requantize_tile<1, 64>(t, acc1, quant_params(sc, true), a.q_out);
         return;
     }
     reduce_tile<SR, 64, 1>(a, t, acc);
