@@ -382,6 +382,24 @@ gq_status gq_units_faults(const gq_units *u, uint64_t *count) {
     return ok();
 }
 
+// Writes the fault count (after the device is idle).
+static gq_status set_faults(const char *op, gq_units *u, bool force) {
+    GQ_TRY(check_units(op, u));
+    uint32_t v = 0;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&v, u->d_faults, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(GQ_ERR_HIP, op, "reading the fault counter failed");
+    v = force ? (v == 0 ? 1u : v) : 0u;
+    if (hipMemcpy(u->d_faults, &v, sizeof v, hipMemcpyHostToDevice) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+        return fail(GQ_ERR_HIP, op, "writing the fault counter failed");
+    return ok();
+}
+
+gq_status gq_units_clear_faults(gq_units *u) { return set_faults("gq_units_clear_faults", u, false); }
+
+gq_status gq_units_force_timeout(gq_units *u) { return set_faults("gq_units_force_timeout", u, true); }
+
 gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units) {
     if (!u) return fail(GQ_ERR_INVALID, "gq_units_info", "unit table is NULL");
     if (n) *n = u->n;

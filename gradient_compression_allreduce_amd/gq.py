@@ -23,6 +23,7 @@ CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_reduce_tile", "gq_units_faults",
+           "gq_units_clear_faults", "gq_units_force_timeout",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
@@ -64,6 +65,10 @@ def _load():
     L.gq_units_reduce_tile.argtypes = [vp, ctypes.POINTER(i64)]
     L.gq_units_faults.restype = st
     L.gq_units_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.gq_units_clear_faults.restype = st
+    L.gq_units_clear_faults.argtypes = [vp]
+    L.gq_units_force_timeout.restype = st
+    L.gq_units_force_timeout.argtypes = [vp]
     L.gq_absmax.restype = st
     L.gq_absmax.argtypes = [vp, i32, i32, f32, vp, vp, vp]
     L.gq_quantize.restype = st
@@ -222,10 +227,25 @@ def gq_units_reduce_tile(units):
 
 
 def gq_units_faults(units):
-    """Bounded waits that gave up on this table (synchronizes; 0 expected)."""
+    """Bounded waits that gave up on this table since it was created or its
+    count was cleared (synchronizes; 0 expected)."""
     c = ctypes.c_uint64(0)
     _check(lib.gq_units_faults(units.handle, ctypes.byref(c)))
     return c.value
+
+
+def gq_units_clear_faults(units):
+    """Set the table's fault count to zero, so that its waits wait normally
+    again (synchronizes)."""
+    _check(lib.gq_units_clear_faults(units.handle))
+
+
+def gq_units_force_timeout(units):
+    """Testing aid: make the fault count nonzero, so that the table's
+    persistent launches take every wait not satisfied at its first look as
+    timed out (counted; outputs may be invalid) until the count is cleared.
+    Synchronizes."""
+    _check(lib.gq_units_force_timeout(units.handle))
 
 
 def gq_absmax(xs, units, amax_bits, in_mul=1.0, stream=None):

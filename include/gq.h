@@ -158,14 +158,38 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems);
 
 /*
- * gq_units_faults -- number of bounded waits that gave up since the table
- * was created.  The persistent kernels size their grid to what the device
- * keeps resident; a wait can only give up (after about a second) if the
- * device did not run the whole grid, e.g. while other long-running work
- * held its compute units.  The results of such a launch are invalid.
- * Synchronizes the device.  count: host pointer receiving the number.
+ * gq_units_faults -- number of bounded waits that gave up on the table
+ * since it was created or its count was last cleared.  The persistent
+ * kernels size their grid to what the device keeps resident; a wait can
+ * only give up (after about a second) if the device did not run the whole
+ * grid, e.g. while other long-running work held its compute units.  The
+ * results of such a launch are invalid.  While the count is nonzero, every
+ * wait on the table gives up at its first unsatisfied look (so a launch in
+ * that state still ends soon, and its outputs may be invalid too): fix the
+ * cause, then clear the count (gq_units_clear_faults) or create a new
+ * table.  Synchronizes the device.  count: host pointer receiving the
+ * number.
  */
 gq_status gq_units_faults(const gq_units *u, uint64_t *count);
+
+/*
+ * gq_units_clear_faults -- sets the table's fault count to zero, so that
+ * its waits wait normally again.  The table's other state needs no repair:
+ * every launch that has ended leaves it consistent, whether or not its
+ * waits gave up.  Synchronizes the device.  Errors: GQ_ERR_INVALID (NULL
+ * table), GQ_ERR_DEVICE (table on another device), GQ_ERR_HIP.
+ */
+gq_status gq_units_clear_faults(gq_units *u);
+
+/*
+ * gq_units_force_timeout -- testing aid for the time-out path: makes the
+ * fault count nonzero (1 if it was 0), so that the persistent launches on
+ * the table (gq_quantize in its fused form, gq_reduce_requantize) take
+ * every wait that is not satisfied at its first look as timed out, count
+ * it, and go on, until the count is cleared.  Their outputs may then be
+ * invalid.  Synchronizes the device.  Errors as gq_units_clear_faults.
+ */
+gq_status gq_units_force_timeout(gq_units *u);
 
 /*
  * gq_absmax -- §2.2.1 max|g| per unit and rank, with g = float(x) * in_mul
@@ -280,7 +304,8 @@ gq_status gq_pipe_slots(const gq_pipe *p, int64_t *slot_elems, int64_t *slot_uni
 
 /*
  * gq_pipe_faults -- bounded waits that gave up in the plan's quantize
- * launches (see gq_units_faults).  Synchronizes the device.
+ * launches (see gq_units_faults; the plan's tables keep their counts, so a
+ * plan with faults is replaced by a new one).  Synchronizes the device.
  */
 gq_status gq_pipe_faults(const gq_pipe *p, uint64_t *count);
 

@@ -130,6 +130,9 @@ def test_argument_errors_before_any_device_call(gq):
     assert L.gq_units_schedule(null, gq.GQ_F32, ctypes.byref(v32)) == gq.GQ_ERR_INVALID
     assert L.gq_units_reduce_tile(null, ctypes.byref(v64)) == gq.GQ_ERR_INVALID
     assert "unit table" in gq.gq_last_error()
+    assert L.gq_units_force_timeout(null) == gq.GQ_ERR_INVALID
+    assert "unit table" in gq.gq_last_error()
+    assert L.gq_units_clear_faults(null) == gq.GQ_ERR_INVALID
 
 
 def test_units_create_rejects_bad_tables(gq):

@@ -334,6 +334,55 @@ def test_graph_replays_match_eager(gq, oracle):
     del g
 
 
+def test_forced_timeout_then_recovery(gq, oracle):
+    """The time-out path, forced from the host: with the table's fault count
+    made nonzero, each persistent launch takes every wait not satisfied at
+    its first look as timed out, counts it and still ends.  Once the count
+    is cleared, the table works normally without being rebuilt: the reduce
+    is exact for the codes a forced quantize left, and a whole step after a
+    forced reduce is exact.  (Whether a wait is unsatisfied at its first
+    look depends on timing, so the give-ups are reported, not required.)"""
+    import torch
+    rng = np.random.default_rng(470)
+    W = 8
+    # hundreds of units of two or three tiles and one of many tiles: the
+    # step has thousands of cross-group waits
+    sizes = [int(v) for v in rng.integers(17_000, 45_000, 300)] + [1_000_003]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, F32) for _ in range(W)]
+    dx = [to_device(x) for x in xs]
+    step = GpuStep(gq, off, W, F32, n)
+    assert gq.gq_units_faults(step.units) == 0
+
+    say("case forced_timeout quantize W", W, "n", n, "units", off.size - 1)
+    gq.gq_units_force_timeout(step.units)
+    assert gq.gq_units_faults(step.units) == 1
+    step.quantize(dx, 1.0)
+    f1 = gq.gq_units_faults(step.units)
+    say("forced quantize: waits timed out", f1 - 1)
+    gq.gq_units_clear_faults(step.units)
+    assert gq.gq_units_faults(step.units) == 0
+    step.reduce(fused=True, with_r=True)
+    got = step.host()
+    r = oracle.reduce_dequant(got["q"], got["scale"], off)
+    s2, q2 = oracle.requantize(r, off)
+    compare_step(got, dict(got, r=r, scale_out=s2, q_out=q2), W, check_r=True,
+                 label="after_forced_quantize")
+
+    say("case forced_timeout reduce")
+    gq.gq_units_force_timeout(step.units)
+    step.reduce(fused=True, with_r=False)
+    f2 = gq.gq_units_faults(step.units)
+    say("forced reduce: waits timed out", f2 - 1)
+    gq.gq_units_clear_faults(step.units)
+    step.quantize(dx, 1.0)
+    step.reduce(fused=True, with_r=True)
+    got = step.host()
+    compare_step(got, oracle.allreduce_step(xs, F32, off, 1.0), W, check_r=True,
+                 label="after_forced_reduce")
+
+
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
 def test_units_on_tile_boundaries(gq, oracle, kind):
     """Units of exactly one, two and three tiles of each geometry (16384 and
