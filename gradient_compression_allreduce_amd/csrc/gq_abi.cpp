@@ -216,8 +216,9 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
     if (!out) return fail(GQ_ERR_INVALID, op, "out is NULL");
     *out = nullptr;
     if (!h_off) return fail(GQ_ERR_INVALID, op, "h_off is NULL");
-    if (n_units < 1 || n_units > (int64_t(1) << 30))
-        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
+    if (n_units < 1 || n_units >= GQ_MAX_TILES)
+        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, %d]", (long long)n_units,
+                    GQ_MAX_TILES - 1);
     if (h_off[0] < 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld < 0", (long long)h_off[0]);
     for (int64_t u = 0; u < n_units; ++u)
         if (h_off[u + 1] <= h_off[u])
@@ -282,6 +283,11 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
         std::vector<int32_t> multi, unit_first;
         build_tiles(off, V, static_cast<int64_t>(t.block) * t.slots, tiles, multi, unit_first,
                     t.n_multi_units, t.max_count);
+        if (static_cast<int64_t>(tiles.size()) >= GQ_MAX_TILES) {
+            (void)gq_units_destroy(U);
+            return fail(GQ_ERR_INVALID, op, "table of %lld work tiles (limit %d): too many units "
+                        "or elements", (long long)tiles.size(), GQ_MAX_TILES - 1);
+        }
         // hot-path split: small units, and the tiles of the others
         std::vector<gq::Tile> small, big;
         int32_t big_max = 1;
@@ -548,8 +554,9 @@ gq_status gq_pipe_create(const int64_t *h_off, int64_t n_units, const int64_t *b
     if (mode != GQ_PIPE_OVERLAP && mode != GQ_PIPE_SERIAL)
         return fail(GQ_ERR_INVALID, op, "unknown mode %d", mode);
     if (!h_off || !bucket_units) return fail(GQ_ERR_INVALID, op, "h_off or bucket_units is NULL");
-    if (n_units < 1 || n_units > (int64_t(1) << 30))
-        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, 2^30]", (long long)n_units);
+    if (n_units < 1 || n_units >= GQ_MAX_TILES)
+        return fail(GQ_ERR_INVALID, op, "n_units = %lld outside [1, %d]", (long long)n_units,
+                    GQ_MAX_TILES - 1);
     if (h_off[0] != 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld, must be 0", (long long)h_off[0]);
     for (int64_t u = 0; u < n_units; ++u)
         if (h_off[u + 1] <= h_off[u])

@@ -19,6 +19,7 @@ GQ_F32, GQ_F16 = 0, 1
 GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
 GQ_PIPE_OVERLAP, GQ_PIPE_SERIAL = 0, 1
 GQ_MAX_RANKS = 64
+GQ_MAX_TILES = 1 << 22
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",

@@ -80,6 +80,12 @@ typedef enum {
 /* Largest number of simulated ranks a call accepts. */
 #define GQ_MAX_RANKS 64
 
+/* Bound (exclusive) on the work tiles of a unit table in any of its slot
+ * geometries (a unit takes at least one tile; long units several).  It
+ * keeps every launch's grid below 2^32 work-items and the tickets a launch
+ * hands out (ranks x tiles + resident work groups) below 2^32. */
+#define GQ_MAX_TILES (1 << 22)
+
 /* A hipStream_t, passed as an opaque pointer. */
 typedef void *gq_stream;
 
@@ -113,6 +119,7 @@ gq_status gq_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
 
 /*
  * gq_units_create -- build a unit table on the current device.
+ * n_units  1 .. GQ_MAX_TILES - 1.
  * h_off    host array of n_units+1 element offsets: h_off[0] >= 0, strictly
  *          increasing; n = h_off[n_units] elements per rank (1 .. 2^40).
  *          Unit u is [h_off[u], h_off[u+1]).  Units may start at any
@@ -122,8 +129,10 @@ gq_status gq_plan_chunks(int64_t numel, int32_t elem_bytes, int64_t chunk_bytes,
  *          concatenate each tensor's gq_plan_chunks offsets.
  * out      receives the table.
  * Allocates device memory (work tables + scratch, about 1 KiB per 32K
- * elements) and synchronizes the device.  Errors: GQ_ERR_INVALID,
- * GQ_ERR_HIP (allocation or copy failed).
+ * elements) and synchronizes the device.  Errors: GQ_ERR_INVALID (also
+ * for a table that would need GQ_MAX_TILES work tiles or more in one of
+ * its slot geometries, from about 3.4e10 elements per rank), GQ_ERR_HIP
+ * (allocation or copy failed).
  */
 gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out);
 

@@ -144,6 +144,11 @@ def test_units_create_rejects_bad_tables(gq):
         assert st == gq.GQ_ERR_INVALID, off
         assert not h.value
     assert L.gq_units_create(None, 1, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+    # unit counts outside [1, GQ_MAX_TILES - 1] are rejected before h_off is read
+    a = np.array([0, 1], dtype=np.int64)
+    for n_units in (0, gq.GQ_MAX_TILES, 1 << 40):
+        assert L.gq_units_create(a.ctypes.data, n_units, ctypes.byref(h)) == gq.GQ_ERR_INVALID
+        assert "n_units" in gq.gq_last_error()
     assert L.gq_units_destroy(None) == gq.GQ_OK
 
 
