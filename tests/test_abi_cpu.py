@@ -217,3 +217,36 @@ def test_pipe_argument_errors(gq):
                           None) == gq.GQ_ERR_INVALID
     assert L.gq_pipe_step(None, x, 2, gq.GQ_F32, 1.0, slots, slots, good, good + 8,
                           None) == gq.GQ_ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: without libgq.so next to it, importing
+    it raises."""
+    import importlib.util
+    import shutil
+    import gradient_compression_allreduce_amd as pkg
+    src = os.path.join(os.path.dirname(pkg.__file__), "gq.py")
+    shutil.copy(src, tmp_path / "gq.py")
+    spec = importlib.util.spec_from_file_location("gq_without_lib", str(tmp_path / "gq.py"))
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="libgq.so is not built"):
+        spec.loader.exec_module(mod)
+
+
+def test_product_sources_never_use_the_oracle():
+    """Nothing under the package (binding, build script, HIP/C++ sources)
+    imports, includes, loads or builds the oracle or the input generators."""
+    import gradient_compression_allreduce_amd as pkg
+    root = os.path.dirname(pkg.__file__)
+    pat = re.compile(r"(import|from)\s+(oracle|datagen)\b|#include\s+.*oracle|liboracle|"
+                     r"oracle[/.]|datagen[/.]")
+    hits = []
+    for d, _, files in os.walk(root):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                path = os.path.join(d, f)
+                with open(path, errors="replace") as fh:
+                    for k, line in enumerate(fh, 1):
+                        if pat.search(line):
+                            hits.append("%s:%d: %s" % (path, k, line.strip()))
+    assert not hits, hits
