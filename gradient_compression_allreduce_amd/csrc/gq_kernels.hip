@@ -64,6 +64,32 @@ constexpr uint32_t kSpinLimit = 1u << 20;       // bounded wait (about a second)
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Streaming accesses.  The hot loops read every input byte once and write
+// every output byte once, so their loads and stores carry the non-temporal
+// hint (the nt bit of global_load/global_store), which keeps read-once and
+// write-once data from competing with other lines in the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(int8_t *p, uint32_t w) {
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t *>(p));
+}
+
+__device__ __forceinline__ void store_stream(int8_t *p, uint32_t w0, uint32_t w1) {
+    const u32x2 v = {w0, w1};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+}
+
+__device__ __forceinline__ void store_stream(int8_t *p, uint4 w) {
+    const u32x4 v = {w.x, w.y, w.z, w.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
 // threadIdx.x as a value the compiler cannot see through, so that per-lane
 // index arithmetic is not hoisted out of the persistent loops (hoisted
 // values stay live across the whole loop and cost registers).
@@ -305,7 +331,7 @@ __device__ __forceinline__ void issue_tile(const void *x, const Tile &t, int64_t
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-            raw[s] = xv[j < jmax ? j : jmax];
+            raw[s] = load_stream(xv + (j < jmax ? j : jmax));
         }
     }
 }
@@ -395,11 +421,11 @@ __device__ __forceinline__ void quantize_slot(const typename In<TIn>::Raw &raw, 
     const int64_t i0 = j * V;
     if constexpr (V == 4) {
         const uint32_t p0 = pk[0];
-        if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint32_t *>(q + i0) = p0;
+        if (i0 >= t.begin && i0 + V <= t.end) store_stream(q + i0, p0);
         else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, 0, 0, 0));
     } else {
         const uint32_t p0 = pk[0], p1 = pk[1];
-        if (i0 >= t.begin && i0 + V <= t.end) *reinterpret_cast<uint2 *>(q + i0) = make_uint2(p0, p1);
+        if (i0 >= t.begin && i0 + V <= t.end) store_stream(q + i0, p0, p1);
         else store_codes_part(q, i0, V, t.begin, t.end, make_uint4(p0, p1, 0, 0));
     }
 }
@@ -952,14 +978,14 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const uint32_t o = o0 + static_cast<uint32_t>(s * BLOCK);
-                    v[r][s] = qv[o < lim ? o : lim];
+                    v[r][s] = load_stream(qv + (o < lim ? o : lim));
                 }
             } else {
                 const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]);
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-                    v[r][s] = qv[j < jmax ? j : jmax];
+                    v[r][s] = load_stream(qv + (j < jmax ? j : jmax));
                 }
             }
         }
@@ -1054,7 +1080,7 @@ __device__ __forceinline__ void requantize_tile_mode(const Tile &t, const float 
         }
         const int64_t i0 = j * RV;
         const uint4 pk = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        if (i0 >= t.begin && i0 + RV <= t.end) *reinterpret_cast<uint4 *>(q + i0) = pk;
+        if (i0 >= t.begin && i0 + RV <= t.end) store_stream(q + i0, pk);
         else store_codes_part(q, i0, RV, t.begin, t.end, pk);
     }
 }
