@@ -34,6 +34,23 @@ constexpr int REPORT_BLOCK = R_BLOCK;  // one work group per reduce-table tile
 constexpr int REPORT_V = 16;
 constexpr uint64_t kAbs64 = 0x7fffffffffffffffull;
 
+// Streaming accesses: the sum reads its inputs once and writes its result
+// once, so its whole-slot loads and stores carry the non-temporal hint (the
+// nt bit).  The report keeps plain loads: it reads a reference and codes
+// that were usually written just before, and the hint made it slower.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(float *p, float a, float b, float c, float d) {
+    const f32x4 v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t b) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(b)));
 }
@@ -80,7 +97,7 @@ __global__ __launch_bounds__(SUM_BLOCK) void k_sum_f32(const SArgs a) {
             const uint4 *xv = static_cast<const uint4 *>(a.x[w0 + r]);
 #pragma unroll
             for (int s = 0; s < SUM_SLOTS; ++s)
-                raw[r][s] = js[s] < nfull ? xv[js[s]] : make_uint4(0, 0, 0, 0);
+                raw[r][s] = js[s] < nfull ? load_stream(xv + js[s]) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < SUM_RG; ++r) {
@@ -123,11 +140,10 @@ __global__ __launch_bounds__(SUM_BLOCK) void k_sum_f32(const SArgs a) {
         }
         const int64_t i0 = js[s] * V;
         if (js[s] < nfull) {
-            float4 *rp = reinterpret_cast<float4 *>(a.r + i0);
 #pragma unroll
             for (int k = 0; k < V / 4; ++k)
-                rp[k] = make_float4(acc[s][4 * k], acc[s][4 * k + 1], acc[s][4 * k + 2],
-                                    acc[s][4 * k + 3]);
+                store_stream(a.r + i0 + 4 * k, acc[s][4 * k], acc[s][4 * k + 1], acc[s][4 * k + 2],
+                             acc[s][4 * k + 3]);
         } else {
             for (int k = 0; k < V; ++k)
                 if (i0 + k < a.n) a.r[i0 + k] = acc[s][k];
