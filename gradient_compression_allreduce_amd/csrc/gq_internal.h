@@ -55,7 +55,7 @@ constexpr int R_SLOTS_NARROW = 1;
 constexpr int R_SLOTS_WIDE = 2;
 
 // Units whose 16-byte slots span at most 64 * SMALL_SLOTS[table] slots are
-// "small": one wave handles a whole unit, in a first phase of the
+// "small": one wave handles a whole unit, in a phase of its own of the
 // persistent kernel, with no tile exchange and no ticket.  Reduce tables
 // with narrow tiles double that span: their waves sum a unit in two halves.
 constexpr int SMALL_SLOTS_Q = 16;    // fp32: 4096 elements, fp16: 8192 elements

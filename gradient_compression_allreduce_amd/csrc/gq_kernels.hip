@@ -604,8 +604,12 @@ __device__ __forceinline__ void quantize_small_unit(const QArgs &a, int64_t item
     quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
 }
 
-// First phase of the persistent kernels: wave v of work group g takes the
-// small items v + waves * (g + G * k).  Ends with a work-group barrier.
+// The small units' phase of the persistent kernels: wave v of work group g
+// takes the small items v + waves * (g + G * k).  Ends with a work-group
+// barrier.  The quantize kernels and the narrow reduce run it after their
+// ticket loop, so that it fills the ragged end of the tile phase instead of
+// holding back the first tiles; the wide reduce runs it first (run last,
+// it made that kernel slower).
 template <int BLOCK, typename F>
 __device__ __forceinline__ void small_phase(int64_t items, F &&one) {
     constexpr int WPG = BLOCK / 64;
@@ -626,9 +630,6 @@ template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_chunk(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
-    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
-        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
-    });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, ticket
     const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
@@ -694,6 +695,9 @@ void k_quantize_chunk(const QArgs a) {
             tn = next_ticket();
         }
     }
+    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
+        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+    });
     launch_exit(a.ctl);
 }
 
@@ -712,9 +716,6 @@ template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_layer(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
-    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
-        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
-    });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[3];  // unit max, ticket, polled-ready flag
     __shared__ Raw park[S][BLOCK];
@@ -863,6 +864,9 @@ void k_quantize_layer(const QArgs a) {
             has_c = true;
         }
     }
+    small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
+        quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+    });
     launch_exit(a.ctl);
 }
 
@@ -1183,8 +1187,6 @@ void k_reduce_coop(const RArgs a) {
     // the small phase's half-unit sums: 8 KiB per wave
     __shared__ float4 spark[(BLOCK / 64) * SMALL_SLOTS_R * (RV / 4) * 64];
     float4 *wpark = spark + (threadIdx.x >> 6) * (SMALL_SLOTS_R * (RV / 4) * 64);
-    small_phase<BLOCK>(a.n_small,
-                       [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R, true>(a, item, wpark); });
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, next ticket
     const int64_t total = a.n_tiles;
@@ -1248,6 +1250,8 @@ void k_reduce_coop(const RArgs a) {
         arr_c = arr_n;
         tk = tn;
     }
+    small_phase<BLOCK>(a.n_small,
+                       [&](int64_t item) { reduce_small_unit<SMALL_SLOTS_R, true>(a, item, wpark); });
     launch_exit(a.ctl);
 }
 
@@ -1455,8 +1459,8 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
     constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
     const int64_t resident = resident_groups<coop>(BLOCK);
     if (resident >= t.big_max_count) {
-        // one launch: small units first (one wave each), then the tiles of
-        // the others through the ticket counter
+        // one launch: the tiles of the other units through the ticket
+        // counter, then the small units (one wave each)
         QArgs c = a;
         c.tiles = t.d_big;
         c.n_tiles = t.n_big;
