@@ -250,3 +250,27 @@ def test_product_sources_never_use_the_oracle():
                         if pat.search(line):
                             hits.append("%s:%d: %s" % (path, k, line.strip()))
     assert not hits, hits
+
+
+def test_bench_traffic_follows_the_kernel_source(monkeypatch):
+    """The bench reports measured traffic only from a counter summary taken
+    on the current kernel source; any other summary reads as unmeasured."""
+    import bench
+    names = [f for f in os.listdir(bench.PROFILES) if f.startswith("traffic_")]
+    assert names, "no counter summaries committed"
+    current = bench.kernel_source_hash()
+    for name in names:
+        kernel, workload = re.match(r"traffic_(k_quantize_layer|k_quantize_chunk|k_reduce_coop_wide|k_reduce_coop)_(\w+)\.txt$", name).groups()
+        text = open(os.path.join(bench.PROFILES, name)).read()
+        taken_on = re.search(r"kernel_source_sha256_16 = (\w+)", text).group(1)
+        got = bench.measured_traffic(kernel, workload)
+        if taken_on == current:
+            want = int(re.search(r"traffic_bytes_per_launch = (\d+)", text).group(1))
+            assert got == want, name
+        else:
+            assert got is None, name
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    for name in names:
+        kernel, workload = re.match(r"traffic_(k_quantize_layer|k_quantize_chunk|k_reduce_coop_wide|k_reduce_coop)_(\w+)\.txt$", name).groups()
+        assert bench.measured_traffic(kernel, workload) is None
+    assert bench.measured_traffic("k_quantize_layer", "no_such_workload") is None
