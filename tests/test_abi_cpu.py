@@ -274,3 +274,25 @@ def test_bench_traffic_follows_the_kernel_source(monkeypatch):
         kernel, workload = re.match(r"traffic_(k_quantize_layer|k_quantize_chunk|k_reduce_coop_wide|k_reduce_coop)_(\w+)\.txt$", name).groups()
         assert bench.measured_traffic(kernel, workload) is None
     assert bench.measured_traffic("k_quantize_layer", "no_such_workload") is None
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/gq.h is a C header: it compiles as strict C99, warnings as
+    errors, and every entry point it declares can be referenced from C."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    header = os.path.join(ROOT, "include", "gq.h")
+    names = re.findall(r"^gq_status (gq_\w+)\(|^const char \*(gq_\w+)\(", open(header).read(), re.M)
+    names = [a or b for a, b in names]
+    assert len(names) >= 20
+    src = tmp_path / "use.c"
+    src.write_text('#include "gq.h"\ntypedef void (*fn)(void);\nfn table[] = {%s};\n'
+                   'int main(void) { return (int)(sizeof table == 0); }\n'
+                   % ", ".join("(fn)%s" % n for n in names))
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o", str(tmp_path / "use.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
