@@ -633,6 +633,13 @@ gq_status gq_pipe_faults(const gq_pipe *p, uint64_t *count) {
     return ok();
 }
 
+gq_status gq_pipe_clear_faults(gq_pipe *p) {
+    const char *op = "gq_pipe_clear_faults";
+    if (!p) return fail(GQ_ERR_INVALID, op, "plan is NULL");
+    for (gq_units *u : p->tab) GQ_TRY(gq_units_clear_faults(u));
+    return ok();
+}
+
 gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt, float in_mul,
                        int8_t *const *q_slot, float *const *scale_slot, float *scale_out,
                        int8_t *q_out, gq_stream stream) {

@@ -28,7 +28,7 @@ EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
-           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_step", "gq_chunker_create",
+           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_clear_faults", "gq_pipe_step", "gq_chunker_create",
            "gq_chunker_destroy", "gq_chunker_update", "gq_chunker_predict", "gq_chunker_plan")
 GQ_STATS = 10
 STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
@@ -88,6 +88,8 @@ def _load():
     L.gq_pipe_slots.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.gq_pipe_faults.restype = st
     L.gq_pipe_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.gq_pipe_clear_faults.restype = st
+    L.gq_pipe_clear_faults.argtypes = [vp]
     L.gq_pipe_step.restype = st
     L.gq_pipe_step.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp, vp, vp]
     L.gq_chunker_create.restype = st
@@ -357,6 +359,11 @@ def gq_pipe_faults(pipe):
     c = ctypes.c_uint64(0)
     _check(lib.gq_pipe_faults(pipe.handle, ctypes.byref(c)))
     return c.value
+
+
+def gq_pipe_clear_faults(pipe):
+    """gq_units_clear_faults on each of the plan's tables (synchronizes)."""
+    _check(lib.gq_pipe_clear_faults(pipe.handle))
 
 
 def gq_pipe_step(pipe, xs, q_slots, scale_slots, scale_out, q_out, in_mul=1.0, stream=None):

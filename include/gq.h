@@ -312,11 +312,18 @@ gq_status gq_pipe_destroy(gq_pipe *p);
 gq_status gq_pipe_slots(const gq_pipe *p, int64_t *slot_elems, int64_t *slot_units);
 
 /*
- * gq_pipe_faults -- bounded waits that gave up in the plan's quantize
- * launches (see gq_units_faults; the plan's tables keep their counts, so a
- * plan with faults is replaced by a new one).  Synchronizes the device.
+ * gq_pipe_faults -- bounded waits that gave up in the plan's persistent
+ * launches (see gq_units_faults; the plan's tables keep their counts until
+ * gq_pipe_clear_faults).  Synchronizes the device.
  */
 gq_status gq_pipe_faults(const gq_pipe *p, uint64_t *count);
+
+/*
+ * gq_pipe_clear_faults -- gq_units_clear_faults on each of the plan's
+ * tables.  Synchronizes the device.  Errors: GQ_ERR_INVALID (NULL plan),
+ * GQ_ERR_DEVICE, GQ_ERR_HIP.
+ */
+gq_status gq_pipe_clear_faults(gq_pipe *p);
 
 /*
  * gq_pipe_step -- the whole per-device step (the codes and scales of every

@@ -133,6 +133,8 @@ def test_argument_errors_before_any_device_call(gq):
     assert L.gq_units_force_timeout(null) == gq.GQ_ERR_INVALID
     assert "unit table" in gq.gq_last_error()
     assert L.gq_units_clear_faults(null) == gq.GQ_ERR_INVALID
+    assert L.gq_pipe_clear_faults(null) == gq.GQ_ERR_INVALID
+    assert "plan" in gq.gq_last_error()
 
 
 def test_units_create_rejects_bad_tables(gq):

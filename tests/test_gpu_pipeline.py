@@ -55,6 +55,8 @@ def run_pipe(gq, pipe, xs, W, in_mul, n, U, reps=1, fresh=None):
         gq.gq_pipe_step(pipe, dx, q_slots, s_slots, s_out, q_out, in_mul=in_mul)
     torch.cuda.synchronize()
     assert gq.gq_pipe_faults(pipe) == 0
+    gq.gq_pipe_clear_faults(pipe)
+    assert gq.gq_pipe_faults(pipe) == 0
     return (s_out.cpu().numpy(), q_out.cpu().numpy(), [t.cpu().numpy() for t in q_slots],
             [t.cpu().numpy() for t in s_slots])
 
