@@ -35,7 +35,9 @@
  *     aligned; scale and max buffers 4-byte aligned.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously: outputs are valid once the stream has reached
- *     that point.  Nothing here synchronizes except gq_units_create/destroy.
+ *     that point.  The compute calls never synchronize; creating and
+ *     destroying tables and plans, and the fault queries and resets, do
+ *     (each says so).
  *   - Buffers are owned by the caller and only borrowed while the enqueued
  *     work runs.  The library never allocates in the compute calls.
  *   - A unit table holds scratch memory: calls that use the same table must
