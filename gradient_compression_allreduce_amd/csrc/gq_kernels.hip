@@ -15,10 +15,10 @@
 // work groups (G) than the device keeps resident at once.  Work groups take
 // tiles in order from a ticket counter (tickets run over rank 0's tiles in
 // unit order, then rank 1's, and so on), so the tiles of one unit start at
-// about the same time.  A
-// unit larger than one tile combines its tiles' maxima in device memory
-// (see "cross-work-group max" below) and each of its tiles waits, bounded,
-// for the others, so every input byte is read from HBM once.  A work group
+// about the same time.  A unit larger than one tile combines its tiles'
+// maxima in device memory (see "cross-work-group max" below) and each of
+// its tiles waits, bounded, for the others, so every input byte is read
+// from HBM once.  A work group
 // blocks only in that wait, and by then it has published every tile it
 // holds.  So if all running work groups were blocked, the earliest unit any
 // of them waits on would have all of its taken tiles published and at least
@@ -32,8 +32,10 @@
 // kernels side by side could each hold compute units the other needs, so
 // where two stages may overlap (the bucket pipeline) one of them runs in
 // its wait-free form.  Every wait is bounded: if one ever gives up (the
-// device did not run the grid), a fault counter records it and the
-// launch's results are invalid.
+// device did not run the grid), the table's fault counter records it and
+// the launch's results are invalid.  While that count is nonzero, every
+// wait on the table gives up at its first unsatisfied look, so no later
+// launch waits a second per tile; the host clears the count.
 //
 // Numerics (must match the CPU oracle bit for bit):
 //   * g = x * in_mul is one rounded binary32 multiply (skipped when
@@ -555,7 +557,8 @@ __device__ __forceinline__ uint32_t unit_max(uint64_t *pub, uint64_t *res, int32
                                              uint32_t *faults) {
     const int lane = threadIdx.x;
     const uint64_t arrived = __shfl(arrived_lane0, 0, 64);
-    // after a wait has given up once, later waits do not wait again
+    // once a wait on the table has given up (a nonzero count), later waits
+    // do not wait again until the host clears the count
     const bool give_up = __hip_atomic_load(faults, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
     if (arrived % static_cast<uint64_t>(count) != 0) {
         uint32_t um = 0;
@@ -621,10 +624,10 @@ __device__ __forceinline__ void small_phase(int64_t items, F &&one) {
 }
 
 // Hot path, SCHED_CHUNK: every tile of every rank, one read of the input.
-// Per tile, a work group: issues the loads of its next tile; writes the codes of its
-// current tile (whose unit max it already has), so the loads are in flight
-// during the code pass; takes the next tile's max, publishes it and waits
-// for that unit's max; then takes a new ticket.  It blocks only while
+// Per tile, a work group: issues the loads of its next tile; writes the
+// codes of its current tile (whose unit max it already has), so the loads
+// are in flight during the code pass; takes the next tile's max, publishes
+// it and waits for that unit's max; then takes a new ticket.  It blocks only while
 // holding no unpublished tile and no untaken-but-unstarted ticket.
 template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
