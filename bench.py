@@ -11,9 +11,17 @@ resident in HBM:
 The chunk plans and unit tables are built once at set-up (they depend only
 on the tensor shapes).
 
-Prints one JSON line.  The default workload is the ResNet-152 gradient set
-(W = 8 ranks, 467 fp32 layer tensors, one scale per layer tensor, 25 MiB
-buckets); --workload picks another of the five synthetic workloads.
+Prints one JSON line.  The default workload is the largest one: W = 16
+ranks, each holding one fp32 gradient of 2^28 elements (1 GiB) with
+Student-t(3) values, one scale per 128 KiB chunk (8,192 chunks); --workload
+picks another of the five synthetic workloads.
+
+Every run also checks what it timed: the outputs of the last timed step
+(every rank's scales and codes, the requantized scales and codes) and the
+fp32 rank-order sum of one more reduce are compared with the CPU oracle on
+every element, unit range by unit range, on the same host inputs; that
+oracle pass is timed on one host core and reported as the CPU baseline.  A
+mismatch makes the run exit with status 4.
 """
 import argparse
 import hashlib
@@ -112,33 +120,105 @@ def host_cpu_model():
     return None
 
 
-def cpu_baseline(w, xs, off, kind, min_seconds=10.0, max_reps=20):
-    """The oracle as it stands (single-threaded C), on the same host inputs,
-    pinned to one host core; the whole workload is repeated until about
-    `min_seconds` of CPU work have been timed."""
+def unit_batches(off, min_elems):
+    """Consecutive unit ranges [ua, ub) of at least min_elems elements each
+    (the last one may be shorter).  Units are independent, so the oracle's
+    result on a range of whole units is its result on the whole workload,
+    restricted to that range."""
+    U = off.size - 1
+    out, ua = [], 0
+    while ua < U:
+        ub = int(np.searchsorted(off, off[ua] + min_elems, side="left"))
+        ub = min(max(ub, ua + 1), U)
+        out.append((ua, ub))
+        ua = ub
+    return out
+
+
+def f32_mismatches(a, b):
+    """Elements of two float32 arrays that differ bitwise (NaNs compared by
+    NaN-ness only)."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    na, nb = np.isnan(a), np.isnan(b)
+    bad = (na != nb) | (~na & ~nb & (a.view(np.uint32) != b.view(np.uint32)))
+    return int(np.count_nonzero(bad))
+
+
+def input_checksums(w, xs):
+    """64-bit FNV-1a of every rank's host input buffer (hex), taken in
+    parallel host threads (the C checksum releases the interpreter)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(16, len(xs)))) as ex:
+        return ["%016x" % c for c in ex.map(w.checksum, xs)]
+
+
+def oracle_check(w, xs, off, kind, got, min_seconds=10.0, max_reps=20, batch_elems=1 << 23):
+    """Run the oracle (single-threaded C, as it stands) on the same host
+    inputs, unit range by unit range, one host thread pinned to one core,
+    and compare its outputs with the GPU's on every element.
+
+    got: host-side access to the GPU outputs: got["scale"][w] (numpy, all
+    units), got["scale_out"] (numpy), and callables got["codes"](w, a, b),
+    got["r"](a, b), got["q_out"](a, b) returning element ranges.
+
+    The comparing pass is timed (oracle calls only); if it took less than
+    min_seconds, whole oracle passes are repeated (not compared) until
+    that much CPU work has been timed, and the median is reported."""
     from oracle import Oracle
     o = Oracle()
+    batches = unit_batches(off, batch_elems)
+    bad = {"codes": 0, "scales": 0, "r": 0, "scale_out": 0, "q_out": 0}
+    first_bad = None
     old_aff = os.sched_getaffinity(0)
     core = min(old_aff)
     os.sched_setaffinity(0, {core})
     try:
-        times = []
-        while True:
-            t0 = time.perf_counter()
-            o.allreduce_step(xs, kind, off, w.in_mul)
-            times.append(time.perf_counter() - t0)
-            if sum(times) >= min_seconds or len(times) >= max_reps:
-                break
+        def one_pass(compare):
+            nonlocal first_bad
+            t_sum = 0.0
+            for ua, ub in batches:
+                a, b = int(off[ua]), int(off[ub])
+                loc = off[ua:ub + 1] - a
+                sl = [x[a:b] for x in xs]
+                t0 = time.perf_counter()
+                want = o.allreduce_step(sl, kind, loc, w.in_mul)
+                t_sum += time.perf_counter() - t0
+                if not compare:
+                    continue
+                before = sum(bad.values())
+                for r in range(w.W):
+                    bad["scales"] += f32_mismatches(got["scale"][r][ua:ub], want["scale"][r])
+                    bad["codes"] += int(np.count_nonzero(got["codes"](r, a, b) != want["q"][r]))
+                bad["r"] += f32_mismatches(got["r"](a, b), want["r"])
+                bad["scale_out"] += f32_mismatches(got["scale_out"][ua:ub], want["scale_out"])
+                bad["q_out"] += int(np.count_nonzero(got["q_out"](a, b) != want["q_out"]))
+                if first_bad is None and sum(bad.values()) > before:
+                    first_bad = {"units": [ua, ub], "elements": [a, b]}
+            return t_sum
+
+        times = [one_pass(True)]
+        while sum(times) < min_seconds and len(times) < max_reps:
+            times.append(one_pass(False))
     finally:
         os.sched_setaffinity(0, old_aff)
+    U = off.size - 1
+    compared = {"codes": w.W * w.n, "scales": w.W * U, "r": w.n, "scale_out": U, "q_out": w.n}
+    parity = {"bit_exact": sum(bad.values()) == 0,
+              "elements_compared": int(sum(compared.values())),
+              "compared": compared, "mismatches": bad, "first_mismatch": first_bad,
+              "rule": "bitwise; NaN compared by NaN-ness",
+              "unit_batches": len(batches)}
     dt = float(np.median(times))
     nbytes = w.W * w.n * w.elem_bytes
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    base = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds_per_step": dt, "repetitions": len(times),
             "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
-            "sample": "the whole workload (%d ranks x %d elements), repeated %d times "
-                      "(median): quantize, rank-order reduce and requantize, one host "
-                      "thread pinned to core %d" % (w.W, w.n, len(times), core)}
+            "sample": "the whole workload (%d ranks x %d elements, every unit), in %d unit "
+                      "ranges: quantize, rank-order reduce and requantize; %d pass(es), "
+                      "median; the first pass's outputs are the parity check; one host "
+                      "thread pinned to core %d" % (w.W, w.n, len(batches), len(times), core)}
+    return parity, base
 
 
 def main():
@@ -146,9 +226,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle pass (and with it the parity check of the timed "
+                         "step): for profiling runs only")
     ap.add_argument("--pipeline", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the two-stream bucket pipeline (outside the step)")
     ap.add_argument("--bucket-mib", type=float, default=None,
@@ -191,8 +273,15 @@ def main():
 
     log("workload", w.name, "W", w.W, "n", w.n, "units", U, "chunks", n_chunks)
     t0 = time.perf_counter()
-    xs = [w.fill(r) for r in range(w.W)]
+    xs = []
+    for r in range(w.W):
+        xs.append(w.fill(r))
+        if w.n >= (1 << 26):
+            log("  rank %d generated" % r)
     log("generated inputs in %.1f s" % (time.perf_counter() - t0))
+    t0 = time.perf_counter()
+    checksums = input_checksums(w, xs)
+    log("input checksums in %.1f s" % (time.perf_counter() - t0))
     dev = torch.device("cuda")
     tdt = torch.float32 if kind == 0 else torch.float16
     dx = []
@@ -232,7 +321,13 @@ def main():
         bounds = bucket_bounds(w, gq.gq_plan_chunks,
                                int(args.bucket_mib * 1024 * 1024) if args.bucket_mib else None)
         pipeline = []
-        for mode, name in ((gq.GQ_PIPE_OVERLAP, "overlap"), (gq.GQ_PIPE_SERIAL, "serial")):
+        if bounds.size - 1 < 2:
+            # one tensor larger than a bucket is a bucket of its own: nothing
+            # to pipeline
+            pipeline = {"skipped": "one bucket (a tensor larger than the bucket size is a "
+                                   "bucket of its own)"}
+        for mode, name in (((gq.GQ_PIPE_OVERLAP, "overlap"), (gq.GQ_PIPE_SERIAL, "serial"))
+                           if bounds.size - 1 >= 2 else ()):
             pipe = gq.gq_pipe_create(off, bounds, mode)
             se, su = gq.gq_pipe_slots(pipe)
             q_slots = [torch.empty(se, dtype=torch.int8, device=dev) for _ in range(2 * w.W)]
@@ -346,6 +441,31 @@ def main():
               "min_cos": float(np.min(st[fin, col["cos"]])) if fin.any() else None}
         del ref, stats
 
+    graph = None
+    if args.graph_reps > 0:
+        # the same step, captured once into a HIP graph of graph_reps
+        # repetitions (launch-bound workloads); no allocation or memset is
+        # recorded: the library's compute calls make none
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(args.graph_reps):
+                    gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=cap)
+                    gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=cap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = {"reps": args.graph_reps,
+                 "ms_per_step": round(g0.elapsed_time(g1) / args.graph_reps, 4)}
+        del g
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -374,41 +494,33 @@ def main():
     q_ms = float(np.mean([e_q0[k].elapsed_time(e_q1[k]) for k in range(args.steps)]))
     r_ms = float(np.mean([e_q1[k].elapsed_time(nxt[k]) for k in range(args.steps)]))
     step_ms = [e_q0[k].elapsed_time(nxt[k]) for k in range(args.steps)]
-
-    graph = None
-    if args.graph_reps > 0:
-        # the same step, captured once into a HIP graph of graph_reps
-        # repetitions (launch-bound workloads); no allocation or memset is
-        # recorded: the library's compute calls make none
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for _ in range(args.graph_reps):
-                    gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=cap)
-                    gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=cap)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        g.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph = {"reps": args.graph_reps,
-                 "ms_per_step": round(g0.elapsed_time(g1) / args.graph_reps, 4)}
-        del g
-
-    input_bytes = w.W * w.n * w.elem_bytes
-    value = input_bytes / (ms * 1e-3) / 1e9
-    b_alg = bq + br
-    q_achieved = bq / (q_ms * 1e-3) / 1e9
     faults = gq.gq_units_faults(units)
     if faults:
         print("a bounded cross-group wait gave up %d times: results invalid" % faults,
               file=sys.stderr)
         sys.exit(3)
+
+    # what the last timed step left: every rank's scales and codes and the
+    # requantized output.  One more reduce also writes the fp32 sum; its
+    # requantized output must equal the timed step's.
+    r_sum = None
+    same_again = None
+    if not args.no_cpu_baseline:
+        keep_q, keep_s = q_out.clone(), s_out.clone()
+        r_sum = torch.empty(w.n, dtype=torch.float32, device=dev)
+        gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, r_out=r_sum, stream=stream)
+        torch.cuda.synchronize()
+        same_again = bool(torch.equal(keep_q, q_out)) and bool(
+            torch.equal(keep_s.view(torch.int32), s_out.view(torch.int32)))
+        del keep_q, keep_s
+        if gq.gq_units_faults(units):
+            print("a bounded cross-group wait gave up: results invalid", file=sys.stderr)
+            sys.exit(3)
+
+    input_bytes = w.W * w.n * w.elem_bytes
+    value = input_bytes / (ms * 1e-3) / 1e9
+    b_alg = bq + br
+    q_achieved = bq / (q_ms * 1e-3) / 1e9
     sched = gq.gq_units_schedule(units, gq.GQ_F32 if kind == 0 else gq.GQ_F16)
     qkernel = "k_quantize_chunk" if sched == gq.GQ_SCHED_CHUNK else "k_quantize_layer"
     rkernel = "k_reduce_coop_wide" if gq.gq_units_reduce_tile(units) == 16384 else "k_reduce_coop"
@@ -458,13 +570,30 @@ def main():
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "kernel_source": kernel_source_hash(),
         "wall_s": round(wall, 3),
+        "input_checksums": {"fnv1a64": checksums},
+        "parity": None,
     }
+    ok = True
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on the same inputs ...")
-        rec["cpu_baseline"] = cpu_baseline(w, xs, off, kind)
-        rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 4)
-        rec["cpu_baseline"]["seconds_per_step"] = round(rec["cpu_baseline"]["seconds_per_step"], 3)
+        log("CPU oracle on the same inputs: every element of the timed step ...")
+        t0 = time.perf_counter()
+        got = {"scale": [t.cpu().numpy() for t in scales],
+               "scale_out": s_out.cpu().numpy(),
+               "codes": lambda r, a, b: codes[r][a:b].cpu().numpy(),
+               "r": lambda a, b: r_sum[a:b].cpu().numpy(),
+               "q_out": lambda a, b: q_out[a:b].cpu().numpy()}
+        parity, base = oracle_check(w, xs, off, kind, got)
+        parity["requantized_again_with_sum_identical"] = same_again
+        parity["seconds"] = round(time.perf_counter() - t0, 1)
+        base["value"] = round(base["value"], 4)
+        base["seconds_per_step"] = round(base["seconds_per_step"], 3)
+        rec["parity"] = parity
+        rec["cpu_baseline"] = base
+        ok = parity["bit_exact"] and same_again
+        log("parity:", "bit-exact" if ok else "MISMATCH", parity["mismatches"])
     print(json.dumps(rec), flush=True)
+    if not ok:
+        sys.exit(4)
 
 
 if __name__ == "__main__":

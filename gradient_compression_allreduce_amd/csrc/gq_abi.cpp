@@ -402,6 +402,33 @@ static gq_status set_faults(const char *op, gq_units *u, bool force) {
     return ok();
 }
 
+gq_status gq_units_faults_async(const gq_units *u, uint32_t *count_out, gq_stream stream) {
+    const char *op = "gq_units_faults_async";
+    GQ_TRY(check_ptr(op, "count_out", count_out, 4));
+    GQ_TRY(check_units(op, u));
+    return launch_status(op, gq::launch_copy_word(u->d_faults, count_out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+gq_status gq_units_launch_plan(const gq_units *u, gq_dtype dt, float in_mul, int64_t *q_groups,
+                               int32_t *q_one_launch, int64_t *r_groups, int32_t *r_one_launch) {
+    const char *op = "gq_units_launch_plan";
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    if (!std::isfinite(in_mul) || !(in_mul > 0.0f))
+        return fail(GQ_ERR_INVALID, op, "in_mul = %g must be finite and > 0", (double)in_mul);
+    GQ_TRY(check_units(op, u));
+    const gq::Table &tq = u->tab[q_table(dt)];
+    const gq::Table &tr = u->tab[gq::TAB_R];
+    const int64_t qg = gq::quantize_resident(dt, in_mul != 1.0f, tq);
+    const int64_t rg = gq::reduce_resident(tr);
+    if (qg < 1 || rg < 1) return fail(GQ_ERR_HIP, op, "occupancy query failed");
+    if (q_groups) *q_groups = qg;
+    if (q_one_launch) *q_one_launch = qg >= tq.big_max_count ? 1 : 0;
+    if (r_groups) *r_groups = rg;
+    if (r_one_launch) *r_one_launch = rg >= tr.big_max_count ? 1 : 0;
+    return ok();
+}
+
 gq_status gq_units_clear_faults(gq_units *u) { return set_faults("gq_units_clear_faults", u, false); }
 
 gq_status gq_units_force_timeout(gq_units *u) { return set_faults("gq_units_force_timeout", u, true); }

@@ -202,6 +202,12 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
 hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, bool wait_free,
                          hipStream_t s);
 hipError_t launch_sum_f32(const SArgs &a, gq_dtype dt, hipStream_t s);
+hipError_t launch_copy_word(const uint32_t *src, uint32_t *dst, hipStream_t s);
+// Resident work groups of the persistent kernels a table's fused calls use
+// on the current device (0 if the occupancy query failed): the grid of their
+// one-launch form, which runs when no unit spans more tiles than this.
+int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t);
+int64_t reduce_resident(const Table &t);
 hipError_t launch_error_report(const EArgs &a, hipStream_t s);
 
 }  // namespace gq

@@ -1396,6 +1396,13 @@ __global__ __launch_bounds__(BLOCK) void k_reduce(const RArgs a) {
     requantize_tile<S, BLOCK>(t, acc, quant_params(sc, true), a.q_out);
 }
 
+// Copy of a table's fault count into a caller's buffer, ordered on the
+// caller's stream (a kernel rather than a memory copy, so that it can also
+// be captured into a graph).
+__global__ void k_copy_word(const uint32_t *src, uint32_t *dst) {
+    if (threadIdx.x == 0) dst[0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- launch helpers -------------------------------------------------------------------
 
 struct DeviceInfo {
@@ -1576,6 +1583,29 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
     hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
                        block, 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_copy_word(const uint32_t *src, uint32_t *dst, hipStream_t s) {
+    hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(64), 0, s, src, dst);
+    return hipGetLastError();
+}
+
+template <typename TIn, bool MUL>
+int64_t quantize_resident_typed(const Table &t) {
+    if (t.block == Q_BLOCK_CHUNK)
+        return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_CHUNK, MUL>()>(Q_BLOCK_CHUNK);
+    return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_LAYER, MUL>()>(Q_BLOCK_LAYER);
+}
+
+int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t) {
+    if (dt == GQ_F32)
+        return mul ? quantize_resident_typed<float, true>(t) : quantize_resident_typed<float, false>(t);
+    return mul ? quantize_resident_typed<__half, true>(t) : quantize_resident_typed<__half, false>(t);
+}
+
+int64_t reduce_resident(const Table &t) {
+    if (t.slots == R_SLOTS_WIDE) return resident_groups<coop_reduce_kernel<R_SLOTS_WIDE>()>(R_BLOCK);
+    return resident_groups<coop_reduce_kernel<R_SLOTS_NARROW>()>(R_BLOCK);
 }
 
 hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,

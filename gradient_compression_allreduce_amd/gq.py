@@ -6,8 +6,11 @@ work is enqueued on torch's current stream unless a stream is given.  All
 arithmetic runs in the library's gfx950 kernels; if the library is missing
 the import fails (there is no fallback).
 """
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 import numpy as np
 
@@ -24,7 +27,7 @@ CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_reduce_tile", "gq_units_faults",
-           "gq_units_clear_faults", "gq_units_force_timeout",
+           "gq_units_faults_async", "gq_units_launch_plan", "gq_units_clear_faults", "gq_units_force_timeout",
            "gq_absmax", "gq_quantize",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
@@ -66,6 +69,11 @@ def _load():
     L.gq_units_reduce_tile.argtypes = [vp, ctypes.POINTER(i64)]
     L.gq_units_faults.restype = st
     L.gq_units_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    L.gq_units_faults_async.restype = st
+    L.gq_units_faults_async.argtypes = [vp, vp, vp]
+    L.gq_units_launch_plan.restype = st
+    L.gq_units_launch_plan.argtypes = [vp, i32, f32, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                       ctypes.POINTER(i64), ctypes.POINTER(i32)]
     L.gq_units_clear_faults.restype = st
     L.gq_units_clear_faults.argtypes = [vp]
     L.gq_units_force_timeout.restype = st
@@ -111,6 +119,47 @@ def _load():
 
 lib = _load()
 
+# Tables, plans and chunkers still alive when the interpreter exits are
+# freed here, in an exit hook registered after torch was imported, so it
+# runs before torch's own exit hooks and long before the HIP runtime's
+# teardown at process exit; after it, and whenever the interpreter is
+# already finalizing, the owners' destructors free nothing.
+_live = weakref.WeakSet()
+_closed = False
+
+
+def _release_at_exit():
+    global _closed
+    objs = list(_live)
+    if objs and "torch" in sys.modules:
+        try:
+            torch = sys.modules["torch"]
+            if torch.cuda.is_initialized():
+                torch.cuda.synchronize()
+        except Exception:
+            pass
+    for o in objs:
+        try:
+            o.close()
+        except Exception:
+            pass
+    _closed = True
+
+
+def _register_exit_hook():
+    try:
+        import torch  # noqa: F401  (its exit hooks must run after ours)
+    except ImportError:
+        pass
+    atexit.register(_release_at_exit)
+
+
+_register_exit_hook()
+
+
+def _finalizing():
+    return _closed or sys.is_finalizing()
+
 
 def _check(status):
     if status != GQ_OK:
@@ -134,27 +183,81 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _need(name, t, numel):
-    """Host-side guard: a contiguous device tensor of at least numel
-    elements (the library reads and writes exactly what the call sizes
-    say)."""
-    if not t.is_cuda or not t.is_contiguous() or t.numel() < numel:
-        raise ValueError("%s must be a contiguous device tensor of at least %d elements"
-                         % (name, numel))
+def _current_device():
+    import torch
+    return torch.cuda.current_device()
+
+
+def _need(name, t, numel, dtypes):
+    """Host-side guard, checked before anything is enqueued: a contiguous
+    tensor on the current HIP device, of one of `dtypes`, holding at least
+    numel elements (the library reads and writes exactly what the call's
+    sizes say, so a short or mistyped buffer would be overrun)."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s must be a tensor on the HIP device" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must be of dtype %s, got %s"
+                        % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), numel))
+    if t.device.index != _current_device():
+        raise ValueError("%s is on device %s, the current device is %d"
+                         % (name, t.device, _current_device()))
+
+
+def _need_list(name, ts, W, numel, dtypes):
+    """W tensors, each passing _need."""
+    if not isinstance(ts, (list, tuple)):
+        raise TypeError("%s must be a list of tensors" % name)
+    if len(ts) != W:
+        raise ValueError("%s holds %d tensors for %d ranks" % (name, len(ts), W))
+    for i, t in enumerate(ts):
+        _need("%s[%d]" % (name, i), t, numel, dtypes)
+
+
+def _ranks(name, xs):
+    """Number of ranks of a list of rank buffers (1 .. GQ_MAX_RANKS)."""
+    if not isinstance(xs, (list, tuple)):
+        raise TypeError("%s must be a list of tensors, one per rank" % name)
+    if not 1 <= len(xs) <= GQ_MAX_RANKS:
+        raise ValueError("%s: %d ranks, must be 1 .. %d" % (name, len(xs), GQ_MAX_RANKS))
+    return len(xs)
+
+
+def _grads(xs, numel):
+    """Gradient inputs: 1 .. GQ_MAX_RANKS tensors of one element type
+    (float32 or float16), each of at least numel elements; returns (W,
+    dtype code)."""
+    import torch
+    W = _ranks("xs", xs)
+    dt = getattr(xs[0], "dtype", None)
+    if dt not in (torch.float32, torch.float16):
+        raise TypeError("gradient elements must be float32 or float16, got %s" % dt)
+    _need_list("xs", xs, W, numel, (dt,))
+    return W, (GQ_F32 if dt == torch.float32 else GQ_F16)
+
+
+def _table(units):
+    if not isinstance(units, Units) or not getattr(units, "handle", None):
+        raise ValueError("units must be a live unit table (gq_units_create)")
+    return units
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _i8():
+    import torch
+    return (torch.int8,)
 
 
 def _ptrs(tensors):
     arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
     return ctypes.cast(arr, ctypes.c_void_p), arr
-
-
-def _dtype_code(t):
-    import torch
-    if t.dtype == torch.float32:
-        return GQ_F32
-    if t.dtype == torch.float16:
-        return GQ_F16
-    raise TypeError("gradient elements must be float32 or float16, got %s" % t.dtype)
 
 
 def gq_plan_chunks(numel, elem_bytes, chunk_bytes=CHUNK_BYTES, align_bytes=ALIGN_BYTES):
@@ -182,17 +285,20 @@ class Units:
         self.offsets = off
         self.n = int(off[-1])
         self.n_units = off.size - 1
+        _live.add(self)
 
     @property
     def _as_parameter_(self):
         return self.handle
 
     def close(self):
-        if self.handle:
+        if getattr(self, "handle", None):
             _check(lib.gq_units_destroy(self.handle))
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
+        if _finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -237,6 +343,31 @@ def gq_units_faults(units):
     return c.value
 
 
+def gq_units_faults_async(units, count_out, stream=None):
+    """Enqueue a copy of the table's fault count into count_out (a device
+    int32/uint32 tensor of at least one element) on the stream, without
+    synchronizing; nonzero after the stream's sync means the outputs since
+    the count was last cleared are invalid."""
+    import torch
+    _table(units)
+    _need("count_out", count_out, 1, (torch.int32, torch.uint32))
+    _check(lib.gq_units_faults_async(units.handle, count_out.data_ptr(), _stream(stream)))
+
+
+def gq_units_launch_plan(units, dtype_code=GQ_F32, in_mul=1.0):
+    """{"q_groups", "q_one_launch", "r_groups", "r_one_launch"}: the
+    resident work groups of the table's persistent quantize and reduce
+    kernels on the current device, and whether each stage runs as one
+    persistent launch (True) or in its two-launch form."""
+    _table(units)
+    qg, rg = ctypes.c_int64(0), ctypes.c_int64(0)
+    q1, r1 = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.gq_units_launch_plan(units.handle, dtype_code, in_mul, ctypes.byref(qg),
+                                    ctypes.byref(q1), ctypes.byref(rg), ctypes.byref(r1)))
+    return {"q_groups": qg.value, "q_one_launch": bool(q1.value),
+            "r_groups": rg.value, "r_one_launch": bool(r1.value)}
+
+
 def gq_units_clear_faults(units):
     """Set the table's fault count to zero, so that its waits wait normally
     again (synchronizes)."""
@@ -254,62 +385,92 @@ def gq_units_force_timeout(units):
 def gq_absmax(xs, units, amax_bits, in_mul=1.0, stream=None):
     """amax_bits: int32/uint32 tensor of W*n_units (rank-major), overwritten
     with the bit patterns of max|x*in_mul| per unit."""
+    import torch
+    _table(units)
+    W, dt = _grads(xs, units.n)
+    _need("amax_bits", amax_bits, W * units.n_units, (torch.int32, torch.uint32))
     px, keep = _ptrs(xs)
-    _check(lib.gq_absmax(px, len(xs), _dtype_code(xs[0]), in_mul, units.handle,
-                         amax_bits.data_ptr(), _stream(stream)))
+    _check(lib.gq_absmax(px, W, dt, in_mul, units.handle, amax_bits.data_ptr(),
+                         _stream(stream)))
 
 
 def gq_quantize(xs, units, scales, codes, in_mul=1.0, amax_bits=None, stream=None):
     """Per-unit scales (float32, n_units each) and int8 codes (n each) of W
     gradients xs."""
+    import torch
+    _table(units)
+    W, dt = _grads(xs, units.n)
+    _need_list("scales", scales, W, units.n_units, _f32())
+    _need_list("codes", codes, W, units.n, _i8())
+    if amax_bits is not None:
+        _need("amax_bits", amax_bits, W * units.n_units, (torch.int32, torch.uint32))
     px, k1 = _ptrs(xs)
     ps, k2 = _ptrs(scales)
     pq, k3 = _ptrs(codes)
     am = amax_bits.data_ptr() if amax_bits is not None else None
-    _check(lib.gq_quantize(px, len(xs), _dtype_code(xs[0]), in_mul, units.handle, am,
-                           ps, pq, _stream(stream)))
+    _check(lib.gq_quantize(px, W, dt, in_mul, units.handle, am, ps, pq, _stream(stream)))
+
+
+def _reduce_inputs(codes, scales, units):
+    _table(units)
+    W = _ranks("codes", codes)
+    _need_list("codes", codes, W, units.n, _i8())
+    _need_list("scales", scales, W, units.n_units, _f32())
+    return W
 
 
 def gq_reduce_dequant(codes, scales, units, r_out, stream=None):
+    W = _reduce_inputs(codes, scales, units)
+    _need("r_out", r_out, units.n, _f32())
     pq, k1 = _ptrs(codes)
     ps, k2 = _ptrs(scales)
-    _check(lib.gq_reduce_dequant(pq, ps, len(codes), units.handle, r_out.data_ptr(),
-                                 _stream(stream)))
+    _check(lib.gq_reduce_dequant(pq, ps, W, units.handle, r_out.data_ptr(), _stream(stream)))
 
 
 def gq_requantize(r, units, scale_out, q_out, stream=None):
+    _table(units)
+    _need("r", r, units.n, _f32())
+    _need("scale_out", scale_out, units.n_units, _f32())
+    _need("q_out", q_out, units.n, _i8())
     _check(lib.gq_requantize(r.data_ptr(), units.handle, scale_out.data_ptr(),
                              q_out.data_ptr(), _stream(stream)))
 
 
 def gq_reduce_requantize(codes, scales, units, scale_out, q_out, r_out=None, stream=None):
+    W = _reduce_inputs(codes, scales, units)
+    _need("scale_out", scale_out, units.n_units, _f32())
+    _need("q_out", q_out, units.n, _i8())
+    if r_out is not None:
+        _need("r_out", r_out, units.n, _f32())
     pq, k1 = _ptrs(codes)
     ps, k2 = _ptrs(scales)
     rp = r_out.data_ptr() if r_out is not None else None
-    _check(lib.gq_reduce_requantize(pq, ps, len(codes), units.handle, rp,
-                                    scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))
+    _check(lib.gq_reduce_requantize(pq, ps, W, units.handle, rp, scale_out.data_ptr(),
+                                    q_out.data_ptr(), _stream(stream)))
 
 
 def gq_sum_f32(xs, r_out, in_mul=1.0, mean=False, stream=None):
     """fp32 rank-order sum of the unquantized gradients xs (divided by W if
     mean) into r_out (float32, n)."""
+    _ranks("xs", xs)
     n = xs[0].numel()
-    for i, x in enumerate(xs):
-        _need("xs[%d]" % i, x, n)
-    _need("r_out", r_out, n)
+    W, dt = _grads(xs, n)
+    _need("r_out", r_out, n, _f32())
     px, keep = _ptrs(xs)
-    _check(lib.gq_sum_f32(px, len(xs), _dtype_code(xs[0]), in_mul, n, 1 if mean else 0,
-                          r_out.data_ptr(), _stream(stream)))
+    _check(lib.gq_sum_f32(px, W, dt, in_mul, n, 1 if mean else 0, r_out.data_ptr(),
+                          _stream(stream)))
 
 
 def gq_error_report(q, scale, ref, units, stats_out, stream=None):
     """Per-unit binary64 error statistics of the INT8 result (q, scale)
     against ref; stats_out: float64 tensor of n_units * GQ_STATS, columns
     named by STATS."""
-    _need("q", q, units.n)
-    _need("scale", scale, units.n_units)
-    _need("ref", ref, units.n)
-    _need("stats_out", stats_out, units.n_units * GQ_STATS)
+    import torch
+    _table(units)
+    _need("q", q, units.n, _i8())
+    _need("scale", scale, units.n_units, _f32())
+    _need("ref", ref, units.n, _f32())
+    _need("stats_out", stats_out, units.n_units * GQ_STATS, (torch.float64,))
     _check(lib.gq_error_report(q.data_ptr(), scale.data_ptr(), ref.data_ptr(), units.handle,
                                stats_out.data_ptr(), _stream(stream)))
 
@@ -327,13 +488,16 @@ class Pipe:
         self.n = int(off[-1])
         self.n_units = off.size - 1
         self.n_buckets = bu.size - 1
+        _live.add(self)
 
     def close(self):
-        if self.handle:
+        if getattr(self, "handle", None):
             _check(lib.gq_pipe_destroy(self.handle))
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
+        if _finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -369,23 +533,19 @@ def gq_pipe_clear_faults(pipe):
 def gq_pipe_step(pipe, xs, q_slots, scale_slots, scale_out, q_out, in_mul=1.0, stream=None):
     """Pipelined step over the plan's buckets.  q_slots / scale_slots: lists
     of 2*W tensors (slot s of rank w at index s*W + w)."""
-    W = len(xs)
+    if not isinstance(pipe, Pipe) or not getattr(pipe, "handle", None):
+        raise ValueError("pipe must be a live plan (gq_pipe_create)")
+    W, dt = _grads(xs, pipe.n)
     se, su = gq_pipe_slots(pipe)
-    if len(q_slots) != 2 * W or len(scale_slots) != 2 * W:
-        raise ValueError("need 2*W code slots and 2*W scale slots")
-    for i, x in enumerate(xs):
-        _need("xs[%d]" % i, x, pipe.n)
-    for i, t in enumerate(q_slots):
-        _need("q_slots[%d]" % i, t, se)
-    for i, t in enumerate(scale_slots):
-        _need("scale_slots[%d]" % i, t, su)
-    _need("scale_out", scale_out, pipe.n_units)
-    _need("q_out", q_out, pipe.n)
+    _need_list("q_slots", q_slots, 2 * W, se, _i8())
+    _need_list("scale_slots", scale_slots, 2 * W, su, _f32())
+    _need("scale_out", scale_out, pipe.n_units, _f32())
+    _need("q_out", q_out, pipe.n, _i8())
     px, k1 = _ptrs(xs)
     pq, k2 = _ptrs(q_slots)
     ps, k3 = _ptrs(scale_slots)
-    _check(lib.gq_pipe_step(pipe.handle, px, W, _dtype_code(xs[0]), in_mul, pq, ps,
-                            scale_out.data_ptr(), q_out.data_ptr(), _stream(stream)))
+    _check(lib.gq_pipe_step(pipe.handle, px, W, dt, in_mul, pq, ps, scale_out.data_ptr(),
+                            q_out.data_ptr(), _stream(stream)))
 
 
 class Chunker:
@@ -395,13 +555,16 @@ class Chunker:
         h = ctypes.c_void_p()
         _check(lib.gq_chunker_create(capacity, alpha, default_bytes, ctypes.byref(h)))
         self.handle = h
+        _live.add(self)
 
     def close(self):
-        if self.handle:
+        if getattr(self, "handle", None):
             _check(lib.gq_chunker_destroy(self.handle))
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
+        if _finalizing():
+            return
         try:
             self.close()
         except Exception:

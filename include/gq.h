@@ -169,6 +169,22 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems);
 
 /*
+ * gq_units_launch_plan -- informational: how the fused calls (gq_quantize
+ * with computed maxima for elements of type dt and multiplier in_mul, and
+ * gq_reduce_requantize) run on this table on the current device.
+ * q_groups, r_groups  resident work groups of the persistent quantize and
+ *                     reduce kernels (the grid of their one-launch form);
+ * q_one_launch, r_one_launch  1 if that stage runs as one persistent launch
+ *                     (no unit spans more tiles than the resident groups), 0
+ *                     if it takes the two-launch form.
+ * Any output pointer may be NULL.  Results do not depend on the form.
+ * Errors: GQ_ERR_INVALID (dt, in_mul, NULL table), GQ_ERR_DEVICE,
+ * GQ_ERR_HIP (the occupancy query failed, e.g. no device).
+ */
+gq_status gq_units_launch_plan(const gq_units *u, gq_dtype dt, float in_mul, int64_t *q_groups,
+                               int32_t *q_one_launch, int64_t *r_groups, int32_t *r_one_launch);
+
+/*
  * gq_units_faults -- number of bounded waits that gave up on the table
  * since it was created or its count was last cleared.  The persistent
  * kernels size their grid to what the device keeps resident; a wait can
@@ -182,6 +198,18 @@ gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems);
  * number.
  */
 gq_status gq_units_faults(const gq_units *u, uint64_t *count);
+
+/*
+ * gq_units_faults_async -- the same count, without synchronizing: a copy of
+ * the table's fault count is enqueued on `stream` into count_out (device
+ * memory, one uint32, 4-byte aligned), after the work enqueued before it on
+ * that stream.  Read it once the stream has reached that point (the
+ * caller's usual synchronization).  A nonzero value means that the outputs
+ * of every call on the table since the count was last cleared (or the table
+ * created) are invalid.  Errors: GQ_ERR_INVALID (NULL table or count_out),
+ * GQ_ERR_ALIGN, GQ_ERR_DEVICE, GQ_ERR_HIP.
+ */
+gq_status gq_units_faults_async(const gq_units *u, uint32_t *count_out, gq_stream stream);
 
 /*
  * gq_units_clear_faults -- sets the table's fault count to zero, so that

@@ -108,3 +108,65 @@ def compare_step(got, want, W, check_r=True, check_amax=False, label=""):
     bad = np.flatnonzero(got["q_out"] != want["q_out"])
     assert bad.size == 0, (label, "q_out", int(bad[0]), int(got["q_out"][bad[0]]),
                            int(want["q_out"][bad[0]]), bad.size)
+
+
+def unit_batches(off, min_elems):
+    """Consecutive ranges [ua, ub) of whole units, at least min_elems
+    elements each (the last may be shorter)."""
+    U = off.size - 1
+    out, ua = [], 0
+    while ua < U:
+        ub = int(np.searchsorted(off, off[ua] + min_elems, side="left"))
+        ub = min(max(ub, ua + 1), U)
+        out.append((ua, ub))
+        ua = ub
+    return out
+
+
+def compare_step_streamed(oracle, xs, kind, off, in_mul, step, W, label, batch_elems=1 << 23,
+                          threads=16):
+    """Every element of a GPU step (every rank's scales and codes, the fp32
+    sum, the requantized scales and codes) against the oracle, which runs
+    on ranges of whole units in parallel host threads.  Units are
+    independent, so the oracle's result on a range of whole units is its
+    whole-workload result there.  step.r must hold the sum."""
+    from concurrent.futures import ThreadPoolExecutor
+    batches = unit_batches(off, batch_elems)
+    scales = [s.cpu().numpy() for s in step.scales]
+    s_out = step.scale_out.cpu().numpy()
+
+    def run(ua, ub):
+        a, b = int(off[ua]), int(off[ub])
+        return oracle.allreduce_step([x[a:b] for x in xs], kind, off[ua:ub + 1] - a, in_mul)
+
+    done = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        # a bounded window of batches in flight keeps host memory small
+        window = 2 * threads
+        futs = {}
+        for i in range(min(window, len(batches))):
+            futs[i] = ex.submit(run, *batches[i])
+        for i, (ua, ub) in enumerate(batches):
+            want = futs.pop(i).result()
+            if i + window < len(batches):
+                futs[i + window] = ex.submit(run, *batches[i + window])
+            a, b = int(off[ua]), int(off[ub])
+            where = (label, "units", ua, ub)
+            for r in range(W):
+                assert same_f32(scales[r][ua:ub], want["scale"][r]), where + (
+                    "scale", r, first_mismatch_f32(scales[r][ua:ub], want["scale"][r]))
+                got_q = step.codes[r][a:b].cpu().numpy()
+                bad = np.flatnonzero(got_q != want["q"][r])
+                assert bad.size == 0, where + ("codes", r, a + int(bad[0]), bad.size)
+            got_r = step.r[a:b].cpu().numpy()
+            assert same_f32(got_r, want["r"]), where + ("r", first_mismatch_f32(got_r, want["r"]))
+            assert same_f32(s_out[ua:ub], want["scale_out"]), where + (
+                "scale_out", first_mismatch_f32(s_out[ua:ub], want["scale_out"]))
+            got_q = step.q_out[a:b].cpu().numpy()
+            bad = np.flatnonzero(got_q != want["q_out"])
+            assert bad.size == 0, where + ("q_out", a + int(bad[0]), bad.size)
+            done += b - a
+            if (i + 1) % 8 == 0 or i + 1 == len(batches):
+                say("  compared units [0, %d) of %d (%d elements per rank)"
+                    % (ub, off.size - 1, done))
+    return len(batches)

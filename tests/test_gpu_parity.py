@@ -201,14 +201,28 @@ def test_unit_larger_than_resident_groups(gq, oracle, kind):
 
 
 def test_unit_of_exactly_the_resident_grid(gq, oracle):
-    """A unit of 512 layer tiles (and 512 wide reduce tiles): as many tiles
-    as 256 compute units keep resident work groups, the largest unit the
-    persistent kernels take, so every resident group holds one of its tiles
-    at once; small units around it."""
+    """A unit of exactly as many layer tiles (and wide reduce tiles, both of
+    16384 fp32 elements) as the device keeps the persistent kernels'
+    work groups resident: the largest unit their one-launch form takes, so
+    every resident group holds one of its tiles at once; small units around
+    it.  One tile more takes the two-launch form."""
     rng = np.random.default_rng(27)
-    lens = [300, 512 * 16384, 5000, 7]
+    probe = gq.gq_units_create(np.array([0, 1 << 24], dtype=np.int64))
+    plan = gq.gq_units_launch_plan(probe, gq.GQ_F32, 1.0)
+    G = plan["q_groups"]
+    say("resident groups: quantize", G, "reduce", plan["r_groups"])
+    assert G >= 256 and plan["r_groups"] >= 256
+    lens = [300, G * 16384, 5000, 7]
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     n = int(off[-1])
+    units = gq.gq_units_create(off)
+    assert gq.gq_units_schedule(units, gq.GQ_F32) == gq.GQ_SCHED_LAYER
+    assert gq.gq_units_reduce_tile(units) == 16384
+    plan = gq.gq_units_launch_plan(units, gq.GQ_F32, 1.0)
+    assert plan["q_groups"] == G and plan["q_one_launch"]
+    assert plan["r_one_launch"] == (plan["r_groups"] >= G)
+    over = gq.gq_units_create(np.array([0, (G + 1) * 16384], dtype=np.int64))
+    assert not gq.gq_units_launch_plan(over, gq.GQ_F32, 1.0)["q_one_launch"]
     xs = [_grad(rng, n, F32) for _ in range(2)]
     _run_and_compare(gq, oracle, xs, F32, off, 1.0, "resident_grid_unit", modes=("fused",))
 
@@ -276,8 +290,8 @@ def test_errors_on_device(gq):
     with pytest.raises(gq.GQError) as e:
         gq.gq_quantize([x], units, [s], [q], in_mul=-1.0)
     assert e.value.status == gq.GQ_ERR_INVALID
-    with pytest.raises(gq.GQError) as e:
-        gq.gq_quantize([x[1:]], units, [s], [q])
+    with pytest.raises(gq.GQError) as e:  # 100 elements, 4 bytes past an aligned start
+        gq.gq_quantize([torch.zeros(101, device="cuda")[1:]], units, [s], [q])
     assert e.value.status == gq.GQ_ERR_ALIGN
     torch.cuda.synchronize()
     assert float(s[0]) == 7.0 and int(q[0]) == 5
@@ -355,11 +369,21 @@ def test_forced_timeout_then_recovery(gq, oracle):
     step = GpuStep(gq, off, W, F32, n)
     assert gq.gq_units_faults(step.units) == 0
 
+    # the count read without a device synchronize: a copy enqueued on the
+    # stream after the work, read at the caller's own synchronize
+    cnt = torch.full((2,), 12345, dtype=torch.int32, device="cuda")
+    gq.gq_units_faults_async(step.units, cnt[0:1])
+    torch.cuda.synchronize()
+    assert int(cnt[0]) == 0 and int(cnt[1]) == 12345
+
     say("case forced_timeout quantize W", W, "n", n, "units", off.size - 1)
     gq.gq_units_force_timeout(step.units)
     assert gq.gq_units_faults(step.units) == 1
     step.quantize(dx, 1.0)
+    gq.gq_units_faults_async(step.units, cnt[0:1])
+    torch.cuda.synchronize()
     f1 = gq.gq_units_faults(step.units)
+    assert int(cnt[0]) == f1 >= 1 and int(cnt[1]) == 12345
     say("forced quantize: waits timed out", f1 - 1)
     gq.gq_units_clear_faults(step.units)
     assert gq.gq_units_faults(step.units) == 0
@@ -378,7 +402,9 @@ def test_forced_timeout_then_recovery(gq, oracle):
     gq.gq_units_clear_faults(step.units)
     step.quantize(dx, 1.0)
     step.reduce(fused=True, with_r=True)
+    gq.gq_units_faults_async(step.units, cnt[1:2])
     got = step.host()
+    assert int(cnt[1]) == 0
     compare_step(got, oracle.allreduce_step(xs, F32, off, 1.0), W, check_r=True,
                  label="after_forced_reduce")
 
