@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 SO = os.path.join(LIBDIR, "libgq.so")
-SOURCES = ["gq_abi.cpp", "gq_chunker.cpp", "gq_kernels.hip", "gq_check.hip"]
+SOURCES = ["gq_abi.cpp", "gq_chunker.cpp", "gq_kernels.hip", "gq_check.hip", "gq_noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -497,6 +497,45 @@ gq_status gq_quantize(const void *const *x, int32_t W, gq_dtype dt, float in_mul
     return launch_status(op, gq::launch_quantize(a, dt, t, static_cast<hipStream_t>(stream)));
 }
 
+gq_status gq_quantize_noalloc(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                              const int64_t *h_off, const int64_t *d_off, int64_t n_units,
+                              float *const *scale_out, int8_t *const *q_out, gq_stream stream) {
+    const char *op = "gq_quantize_noalloc";
+    gq::QArgs a;
+    GQ_TRY(fill_qargs(op, x, W, dt, in_mul, a));
+    GQ_TRY(check_ptr_array(op, "scale_out", scale_out, W, 4));
+    GQ_TRY(check_ptr_array(op, "q_out", q_out, W, 16));
+    GQ_TRY(check_ptr(op, "d_off", d_off, 8));
+    if (!h_off) return fail(GQ_ERR_INVALID, op, "h_off is NULL");
+    if (n_units < 1) return fail(GQ_ERR_INVALID, op, "n_units = %lld < 1", (long long)n_units);
+    if (n_units > GQ_NOALLOC_MAX_MAXIMA / W)
+        return fail(GQ_ERR_INVALID, op, "W * n_units = %d * %lld maxima, above the limit of %d",
+                    W, (long long)n_units, GQ_NOALLOC_MAX_MAXIMA);
+    if (h_off[0] < 0) return fail(GQ_ERR_INVALID, op, "h_off[0] = %lld < 0", (long long)h_off[0]);
+    for (int64_t u = 0; u < n_units; ++u)
+        if (h_off[u + 1] <= h_off[u])
+            return fail(GQ_ERR_INVALID, op, "h_off not strictly increasing at unit %lld",
+                        (long long)u);
+    if (h_off[n_units] > (int64_t(1) << 40))
+        return fail(GQ_ERR_INVALID, op, "n = %lld above 2^40", (long long)h_off[n_units]);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    void *sp = gq::noalloc_scratch(dev);
+    if (!sp) return fail(GQ_ERR_HIP, op, "looking up the maxima array on device %d failed", dev);
+    gq::NoallocArgs c;
+    c.x = x;
+    c.scale = scale_out;
+    c.q = q_out;
+    c.d_off = d_off;
+    c.n_units = n_units;
+    c.n = h_off[n_units];
+    c.first = h_off[0];
+    c.in_mul = in_mul;
+    c.dt = dt;
+    c.W = W;
+    return launch_status(op, gq::launch_quantize_noalloc(c, sp, static_cast<hipStream_t>(stream)));
+}
+
 static gq_status fill_rargs(const char *op, const int8_t *const *q, const float *const *scale,
                             int32_t W, gq::RArgs &a) {
     GQ_TRY(check_ranks(op, W));

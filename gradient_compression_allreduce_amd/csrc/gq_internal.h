@@ -203,6 +203,26 @@ hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, bool w
                          hipStream_t s);
 hipError_t launch_sum_f32(const SArgs &a, gq_dtype dt, hipStream_t s);
 hipError_t launch_copy_word(const uint32_t *src, uint32_t *dst, hipStream_t s);
+
+// The no-allocation quantize (gq_noalloc.hip).  Its maxima live in a
+// fixed-size device array of that file; noalloc_scratch returns that
+// array's address on the current device (looked up once per device, with
+// the device current), or nullptr if the lookup failed.
+constexpr int GQ_NOALLOC_MAX_DEVICES = 64;
+struct NoallocArgs {
+    const void *const *x;
+    float *const *scale;
+    int8_t *const *q;
+    const int64_t *d_off;   // [n_units + 1] device copy of the unit offsets
+    int64_t n_units;
+    int64_t n;              // off[n_units]
+    int64_t first;          // off[0]
+    float in_mul;
+    gq_dtype dt;
+    int32_t W;
+};
+void *noalloc_scratch(int device);
+hipError_t launch_quantize_noalloc(const NoallocArgs &a, void *scratch_dev, hipStream_t s);
 // Resident work groups of the persistent kernels a table's fused calls use
 // on the current device (0 if the occupancy query failed): the grid of their
 // one-launch form, which runs when no unit spans more tiles than this.

@@ -23,12 +23,13 @@ GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
 GQ_PIPE_OVERLAP, GQ_PIPE_SERIAL = 0, 1
 GQ_MAX_RANKS = 64
 GQ_MAX_TILES = 1 << 22
+GQ_NOALLOC_MAX_MAXIMA = 1 << 20
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_reduce_tile", "gq_units_faults",
            "gq_units_faults_async", "gq_units_launch_plan", "gq_units_clear_faults", "gq_units_force_timeout",
-           "gq_absmax", "gq_quantize",
+           "gq_absmax", "gq_quantize", "gq_quantize_noalloc",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
            "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_clear_faults", "gq_pipe_step", "gq_chunker_create",
@@ -82,6 +83,8 @@ def _load():
     L.gq_absmax.argtypes = [vp, i32, i32, f32, vp, vp, vp]
     L.gq_quantize.restype = st
     L.gq_quantize.argtypes = [vp, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.gq_quantize_noalloc.restype = st
+    L.gq_quantize_noalloc.argtypes = [vp, i32, i32, f32, vp, vp, i64, vp, vp, vp]
     L.gq_reduce_dequant.restype = st
     L.gq_reduce_dequant.argtypes = [vp, vp, i32, vp, vp, vp]
     L.gq_requantize.restype = st
@@ -409,6 +412,29 @@ def gq_quantize(xs, units, scales, codes, in_mul=1.0, amax_bits=None, stream=Non
     pq, k3 = _ptrs(codes)
     am = amax_bits.data_ptr() if amax_bits is not None else None
     _check(lib.gq_quantize(px, W, dt, in_mul, units.handle, am, ps, pq, _stream(stream)))
+
+
+def gq_quantize_noalloc(xs, h_off, d_off, scales, codes, in_mul=1.0, stream=None):
+    """gq_quantize with computed maxima and no unit table, for callers that
+    cannot allocate device memory: h_off is the host array (int64, numpy) of
+    n_units+1 unit offsets and d_off a device int64 tensor holding the same
+    values.  The library keeps the maxima in a fixed array of its own
+    (W * n_units <= GQ_NOALLOC_MAX_MAXIMA), shared by every call on the
+    device: calls on one device must be ordered."""
+    import torch
+    off = np.ascontiguousarray(h_off, dtype=np.int64)
+    if off.ndim != 1 or off.size < 2:
+        raise ValueError("h_off must hold n_units + 1 >= 2 offsets")
+    U = off.size - 1
+    W, dt = _grads(xs, int(off[-1]))
+    _need("d_off", d_off, U + 1, (torch.int64,))
+    _need_list("scales", scales, W, U, _f32())
+    _need_list("codes", codes, W, int(off[-1]), _i8())
+    px, k1 = _ptrs(xs)
+    ps, k2 = _ptrs(scales)
+    pq, k3 = _ptrs(codes)
+    _check(lib.gq_quantize_noalloc(px, W, dt, in_mul, off.ctypes.data, d_off.data_ptr(), U,
+                                   ps, pq, _stream(stream)))
 
 
 def _reduce_inputs(codes, scales, units):

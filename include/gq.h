@@ -264,6 +264,39 @@ gq_status gq_quantize(const void *const *x, int32_t W, gq_dtype dt, float in_mul
                       gq_stream stream);
 
 /*
+ * gq_quantize_noalloc -- gq_quantize with the maxima computed (amax_bits =
+ * NULL), for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * needs no unit table and allocates nothing: the per-(rank, unit) maxima
+ * live in a fixed array of GQ_NOALLOC_MAX_MAXIMA words (4 MiB) in the
+ * library's device memory, one per device, which every call on that device
+ * shares and which keeps the last call's maxima (each call clears what it
+ * uses first).  Calls on one device therefore must not overlap: enqueue
+ * them on one stream or order them with events; two overlapping calls race
+ * and their outputs are invalid.  Outputs equal gq_quantize's bit for bit.
+ * Its three launches never wait on each other's work groups, and the
+ * inputs are read twice (once for the maxima, once for the codes).
+ * x          host array of W device pointers, n elements of dt each.
+ * h_off      host array of n_units+1 unit offsets, as for gq_units_create
+ *            (h_off[0] >= 0, strictly increasing, n = h_off[n_units] <=
+ *            2^40), checked here.
+ * d_off      a device copy of the same n_units+1 int64 offsets (8-byte
+ *            aligned), read by the kernels while the call runs.  If it
+ *            differs from h_off the outputs are undefined, but every access
+ *            stays inside the buffers h_off describes.
+ * n_units    1 .. GQ_NOALLOC_MAX_MAXIMA / W.
+ * scale_out  host array of W device pointers, each receiving n_units fp32.
+ * q_out      host array of W device pointers, each receiving n int8 codes.
+ * Errors: GQ_ERR_INVALID (W, dt, in_mul, offsets, NULL pointers, or W *
+ * n_units above GQ_NOALLOC_MAX_MAXIMA), GQ_ERR_ALIGN, GQ_ERR_HIP (the
+ * array's address could not be looked up, or a launch failed).
+ */
+#define GQ_NOALLOC_MAX_MAXIMA (1 << 20)
+gq_status gq_quantize_noalloc(const void *const *x, int32_t W, gq_dtype dt, float in_mul,
+                              const int64_t *h_off, const int64_t *d_off, int64_t n_units,
+                              float *const *scale_out, int8_t *const *q_out, gq_stream stream);
+
+/*
  * gq_reduce_dequant -- the INT8 AllReduce reduction of §2.2.1 on one device:
  *   r[i] = (((+0 + q_0[i]*s_0[u]) + q_1[i]*s_1[u]) + ...) + q_{W-1}[i]*s_{W-1}[u]
  * in binary32, each product and each sum rounded (no fused multiply-add),
