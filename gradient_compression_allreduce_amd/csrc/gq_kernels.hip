@@ -375,8 +375,17 @@ __device__ __forceinline__ void small_phase(int64_t items, F &&one) {
 // Per tile, a work group: issues the loads of its next tile; writes the
 // codes of its current tile (whose unit max it already has), so the loads
 // are in flight during the code pass; takes the next tile's max, publishes
-// it and waits for that unit's max; then takes a new ticket.  It blocks only while
-// holding no unpublished tile and no untaken-but-unstarted ticket.
+// it and waits for that unit's max; then moves on to a new ticket.  When the
+// next tile ends its unit (a 128 KiB chunk is one tile), the ticket after it
+// is taken before that tile's loads are issued, so the ticket's round trip
+// overlaps them instead of following them.  Such a tile never waits for
+// another, and the early ticket lies in a later unit than any the work group
+// may then wait on; so a work group blocks only while holding no
+// unpublished tile and no ticket of the unit it waits on or of an earlier
+// one (the scheduling note above then still applies: tickets are taken in
+// order, so the earliest unit anyone waits on has all its tiles taken and
+// published, or an untaken tile and every running work group holding one of
+// its tiles).
 template <typename TIn, int S, int BLOCK, bool MUL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_quantize_chunk(const QArgs a) {
@@ -419,18 +428,33 @@ void k_quantize_chunk(const QArgs a) {
         int wc = static_cast<int>(tk / a.n_tiles);
         int32_t tix = static_cast<int32_t>(tk - static_cast<int64_t>(wc) * a.n_tiles);
         Tile tc = load_desc(a.tiles, tix);
+        // a tile that ends its unit: take the next ticket while its loads fly
+        bool early = tix == tc.first + tc.count - 1;
+        uint32_t pend = 0;
+        if (early && threadIdx.x == 0) pend = take_ticket(a.ctl);
         issue_tile<TIn, S, BLOCK>(a.x[wc], tc, a.n, cur);
         uint32_t mc = tile_max(cur, tc, wc, tix);
-        int64_t tn = next_ticket();
+        auto ticket_after = [&]() -> int64_t {
+            if (!early) return next_ticket();
+            if (threadIdx.x == 0) s_val[1] = pend;
+            __syncthreads();
+            const int64_t t = s_val[1];
+            __syncthreads();
+            return t;
+        };
+        int64_t tn = ticket_after();
         for (;;) {
             const bool more = tn < total;
             int wn = 0;
             int32_t tixn = 0;
             Tile tnx{};
+            early = false;
             if (more) {
                 wn = static_cast<int>(tn / a.n_tiles);
                 tixn = static_cast<int32_t>(tn - static_cast<int64_t>(wn) * a.n_tiles);
                 tnx = load_desc(a.tiles, tixn);
+                early = tixn == tnx.first + tnx.count - 1;
+                if (early && threadIdx.x == 0) pend = take_ticket(a.ctl);
                 issue_tile<TIn, S, BLOCK>(a.x[wn], tnx, a.n, nxt);
             }
             const float sc = __fdiv_rn(In<TIn>::max_value(mc, a.in_mul, MUL), 127.0f);
@@ -443,7 +467,7 @@ void k_quantize_chunk(const QArgs a) {
             tc = tnx;
             wc = wn;
             tix = tixn;
-            tn = next_ticket();
+            tn = ticket_after();
         }
     }
     small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
