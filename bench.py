@@ -110,6 +110,27 @@ def algorithmic_bytes(W, n, e, U):
     return bq, br
 
 
+def stage_kernels(gq, units, kind, in_mul):
+    """Names of the kernels that run the two stages on a table (the form
+    each stage takes decides which)."""
+    dt = gq.GQ_F32 if kind == 0 else gq.GQ_F16
+    plan = gq.gq_units_launch_plan(units, dt, in_mul)
+    if plan["q_form"] == gq.GQ_FORM_SHORT_UNITS:
+        qkernel = "k_quantize_small"
+    elif plan["q_form"] == gq.GQ_FORM_TWO_PASS:
+        qkernel = "k_tile_absmax+k_quantize"
+    else:
+        qkernel = ("k_quantize_chunk" if gq.gq_units_schedule(units, dt) == gq.GQ_SCHED_CHUNK
+                   else "k_quantize_layer")
+    if plan["r_form"] == gq.GQ_FORM_SHORT_UNITS:
+        rkernel = "k_reduce_small"
+    elif plan["r_form"] == gq.GQ_FORM_TWO_PASS:
+        rkernel = "k_reduce"
+    else:
+        rkernel = "k_reduce_coop_wide" if gq.gq_units_reduce_tile(units) == 16384 else "k_reduce_coop"
+    return qkernel, rkernel
+
+
 def host_cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -521,9 +542,7 @@ def main():
     value = input_bytes / (ms * 1e-3) / 1e9
     b_alg = bq + br
     q_achieved = bq / (q_ms * 1e-3) / 1e9
-    sched = gq.gq_units_schedule(units, gq.GQ_F32 if kind == 0 else gq.GQ_F16)
-    qkernel = "k_quantize_chunk" if sched == gq.GQ_SCHED_CHUNK else "k_quantize_layer"
-    rkernel = "k_reduce_coop_wide" if gq.gq_units_reduce_tile(units) == 16384 else "k_reduce_coop"
+    qkernel, rkernel = stage_kernels(gq, units, kind, w.in_mul)
     r_achieved = br / (r_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,

@@ -310,6 +310,11 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
         t.n_small = static_cast<int64_t>(small.size());
         t.n_big = static_cast<int64_t>(big.size());
         t.big_max_count = big_max;
+        {
+            int64_t in_small = 0;
+            for (const gq::Tile &x : small) in_small += x.end - x.begin;
+            t.small_dominant = 2 * in_small > off[n_units] - off[0];
+        }
         e = upload(&t.d_tiles, tiles);
         if (e == hipSuccess) e = upload(&t.d_multi, multi);
         if (e == hipSuccess) e = upload(&t.d_unit_first, unit_first);
@@ -411,7 +416,7 @@ gq_status gq_units_faults_async(const gq_units *u, uint32_t *count_out, gq_strea
 }
 
 gq_status gq_units_launch_plan(const gq_units *u, gq_dtype dt, float in_mul, int64_t *q_groups,
-                               int32_t *q_one_launch, int64_t *r_groups, int32_t *r_one_launch) {
+                               int32_t *q_form, int64_t *r_groups, int32_t *r_form) {
     const char *op = "gq_units_launch_plan";
     if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
     if (!std::isfinite(in_mul) || !(in_mul > 0.0f))
@@ -422,10 +427,14 @@ gq_status gq_units_launch_plan(const gq_units *u, gq_dtype dt, float in_mul, int
     const int64_t qg = gq::quantize_resident(dt, in_mul != 1.0f, tq);
     const int64_t rg = gq::reduce_resident(tr);
     if (qg < 1 || rg < 1) return fail(GQ_ERR_HIP, op, "occupancy query failed");
+    auto form = [](const gq::Table &t, int64_t groups) {
+        if (gq::short_table(t)) return GQ_FORM_SHORT_UNITS;
+        return groups >= t.big_max_count ? GQ_FORM_PERSISTENT : GQ_FORM_TWO_PASS;
+    };
     if (q_groups) *q_groups = qg;
-    if (q_one_launch) *q_one_launch = qg >= tq.big_max_count ? 1 : 0;
+    if (q_form) *q_form = form(tq, qg);
     if (r_groups) *r_groups = rg;
-    if (r_one_launch) *r_one_launch = rg >= tr.big_max_count ? 1 : 0;
+    if (r_form) *r_form = form(tr, rg);
     return ok();
 }
 

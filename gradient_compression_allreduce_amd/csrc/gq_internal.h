@@ -84,6 +84,7 @@ struct Table {
     int64_t n_big = 0;              // tiles of the other units
     Tile *d_big = nullptr;          // [n_big], unit order (first: index into d_big)
     int32_t big_max_count = 1;      // largest tile count of a unit in d_big
+    bool small_dominant = false;    // small units hold most elements
     int32_t *d_multi = nullptr;     // [n_multi] indices of multi tiles
     uint32_t *d_partial = nullptr;  // [GQ_MAX_RANKS][n_tiles] per-tile maxima
     int32_t *d_unit_first = nullptr;  // [n_units+1] first tile of each unit
@@ -92,6 +93,11 @@ struct Table {
     uint64_t *d_cnt = nullptr;      // [GQ_MAX_RANKS][n_multi_units] arrivals
     uint32_t *d_ctl = nullptr;      // [4]: launch epoch, exited work groups, next ticket
 };
+
+// Tables of short units: every unit fits one tile and the small units (one
+// wave each) hold most elements.  Their fused stages need no exchange of
+// maxima and run as wait-free launches instead of a persistent kernel.
+inline bool short_table(const Table &t) { return t.big_max_count == 1 && t.small_dominant; }
 
 // Every array a launcher may hand to a kernel is present and sized for the
 // table (launchers check this before launching anything).

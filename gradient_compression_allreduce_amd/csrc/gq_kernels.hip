@@ -879,8 +879,9 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
 // halves, the first half's sums parked meanwhile in this wave's 8 KiB of
 // LDS (slot group g of lane l at wpark[g * 64 + l]; each lane reads back
 // only its own), and both halves are requantized with the whole unit's
-// scale.
-template <int SR, bool HALVES>
+// scale.  Multi-slot units load RGW ranks ahead (one in the persistent
+// kernels, whose registers are sized for whole tiles).
+template <int SR, bool HALVES, int RGW = 1>
 __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, float4 *wpark) {
     const Tile t = load_desc(a.small, item);
     float acc[SR][RV];
@@ -893,7 +894,7 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
             Tile th = t;
             if (h == 0) th.end = half_end;
             else th.begin = half_end;
-            reduce_tile<SR, 64, 1>(a, th, acc);
+            reduce_tile<SR, 64, RGW>(a, th, acc);
             if (a.r) store_sum<SR, 64>(th, acc, a.r);
             m = umax(m, acc_absmax<SR>(acc));
             if (h == 0) {
@@ -943,7 +944,7 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
         requantize_tile<1, 64>(t, acc1, quant_params(sc, true), a.q_out);
         return;
     }
-    reduce_tile<SR, 64, 1>(a, t, acc);
+    reduce_tile<SR, 64, RGW>(a, t, acc);
     if (a.r) store_sum<SR, 64>(t, acc, a.r);
     const uint32_t m = wave_max(acc_absmax<SR>(acc));
     const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
@@ -1132,6 +1133,35 @@ void k_reduce_coop_wide(const RArgs a) {
     launch_exit(a.ctl);
 }
 
+// Tables whose units all fit one tile and whose small units hold most of
+// the elements (many short tensors): the small units take one wave per
+// (rank, unit) item in a plain launch whose work groups never wait on each
+// other (the few other units take one work group per tile, k_quantize or
+// k_reduce).  With no tile path beside them, these kernels need fewer
+// registers than the persistent ones, so more waves are resident, each
+// wave's unit is its only item (no unit waits for the one before it on the
+// same wave), and the reduce keeps eight ranks' codes in flight for units
+// of more than one slot per lane.
+constexpr int SMALL_BLOCK = 256;
+
+template <typename TIn, bool MUL>
+__global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= static_cast<int64_t>(a.W) * a.n_small) return;
+    quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+}
+
+template <bool HALVES>
+__global__ __launch_bounds__(SMALL_BLOCK) void k_reduce_small(const RArgs a) {
+    __shared__ float4 spark[HALVES ? (SMALL_BLOCK / 64) * SMALL_SLOTS_R * (RV / 4) * 64 : 1];
+    float4 *wpark = spark + (HALVES ? (threadIdx.x >> 6) * (SMALL_SLOTS_R * (RV / 4) * 64) : 0);
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= a.n_small) return;
+    reduce_small_unit<SMALL_SLOTS_R, HALVES, 4>(a, item, wpark);
+}
+
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
 
 // Non-persistent reduce: the plain sum (R_SUM), and the two-launch form
@@ -1238,6 +1268,23 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
         hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
         return hipGetLastError();
     }
+    if (short_table(t)) {
+        // many short tensors: no exchange needed (see k_quantize_small)
+        if (t.n_small > 0) {
+            const int64_t items = static_cast<int64_t>(a.W) * t.n_small;
+            hipLaunchKernelGGL((k_quantize_small<TIn, MUL>),
+                               dim3(static_cast<unsigned>((items + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64))),
+                               dim3(SMALL_BLOCK), 0, s, a);
+        }
+        if (t.n_big > 0) {
+            QArgs c = a;
+            c.tiles = t.d_big;
+            c.n_tiles = t.n_big;
+            hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_FUSED>),
+                               dim3(static_cast<unsigned>(t.n_big), static_cast<unsigned>(a.W)), block, 0, s, c);
+        }
+        return hipGetLastError();
+    }
     constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
     const int64_t resident = resident_groups<coop>(BLOCK);
     if (resident >= t.big_max_count) {
@@ -1331,6 +1378,24 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
         a.list = nullptr;
         hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
                            block, 0, s, a);
+        return hipGetLastError();
+    }
+    if (requantize && short_table(t)) {
+        // many short tensors: no exchange needed (see k_reduce_small)
+        if (t.n_small > 0) {
+            RArgs c = a;
+            c.small = t.d_small;
+            c.n_small = t.n_small;
+            const unsigned groups = static_cast<unsigned>((t.n_small + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
+            if (S == R_SLOTS_NARROW) hipLaunchKernelGGL(k_reduce_small<true>, dim3(groups), dim3(SMALL_BLOCK), 0, s, c);
+            else hipLaunchKernelGGL(k_reduce_small<false>, dim3(groups), dim3(SMALL_BLOCK), 0, s, c);
+        }
+        if (t.n_big > 0) {
+            RArgs c = a;
+            c.tiles = t.d_big;
+            c.n_tiles = t.n_big;
+            hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_big)), block, 0, s, c);
+        }
         return hipGetLastError();
     }
     constexpr auto coop = coop_reduce_kernel<S>();

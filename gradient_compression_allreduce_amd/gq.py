@@ -21,6 +21,7 @@ GQ_OK, GQ_ERR_INVALID, GQ_ERR_ALIGN, GQ_ERR_CAPACITY, GQ_ERR_HIP, GQ_ERR_DEVICE 
 GQ_F32, GQ_F16 = 0, 1
 GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
 GQ_PIPE_OVERLAP, GQ_PIPE_SERIAL = 0, 1
+GQ_FORM_PERSISTENT, GQ_FORM_TWO_PASS, GQ_FORM_SHORT_UNITS = 0, 1, 2
 GQ_MAX_RANKS = 64
 GQ_MAX_TILES = 1 << 22
 GQ_NOALLOC_MAX_MAXIMA = 1 << 20
@@ -358,17 +359,15 @@ def gq_units_faults_async(units, count_out, stream=None):
 
 
 def gq_units_launch_plan(units, dtype_code=GQ_F32, in_mul=1.0):
-    """{"q_groups", "q_one_launch", "r_groups", "r_one_launch"}: the
-    resident work groups of the table's persistent quantize and reduce
-    kernels on the current device, and whether each stage runs as one
-    persistent launch (True) or in its two-launch form."""
+    """{"q_groups", "q_form", "r_groups", "r_form"}: the resident work
+    groups of the table's persistent quantize and reduce kernels on the
+    current device, and the form each fused stage takes (GQ_FORM_*)."""
     _table(units)
     qg, rg = ctypes.c_int64(0), ctypes.c_int64(0)
-    q1, r1 = ctypes.c_int32(0), ctypes.c_int32(0)
+    qf, rf = ctypes.c_int32(-1), ctypes.c_int32(-1)
     _check(lib.gq_units_launch_plan(units.handle, dtype_code, in_mul, ctypes.byref(qg),
-                                    ctypes.byref(q1), ctypes.byref(rg), ctypes.byref(r1)))
-    return {"q_groups": qg.value, "q_one_launch": bool(q1.value),
-            "r_groups": rg.value, "r_one_launch": bool(r1.value)}
+                                    ctypes.byref(qf), ctypes.byref(rg), ctypes.byref(rf)))
+    return {"q_groups": qg.value, "q_form": qf.value, "r_groups": rg.value, "r_form": rf.value}
 
 
 def gq_units_clear_faults(units):

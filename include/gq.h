@@ -174,15 +174,27 @@ gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems);
  * gq_reduce_requantize) run on this table on the current device.
  * q_groups, r_groups  resident work groups of the persistent quantize and
  *                     reduce kernels (the grid of their one-launch form);
- * q_one_launch, r_one_launch  1 if that stage runs as one persistent launch
- *                     (no unit spans more tiles than the resident groups), 0
- *                     if it takes the two-launch form.
+ * q_form, r_form      the form each stage takes:
+ *   GQ_FORM_PERSISTENT   one persistent launch whose work groups combine a
+ *                        long unit's tile maxima (no unit spans more tiles
+ *                        than the resident groups); every input read once;
+ *   GQ_FORM_TWO_PASS     per-tile maxima, then a pass that reads the tiles
+ *                        of the long units again (a unit spans more tiles
+ *                        than the resident groups);
+ *   GQ_FORM_SHORT_UNITS  tables of short units (every unit fits one tile,
+ *                        and units of one wave's share hold most elements):
+ *                        wait-free launches, one wave per (rank, unit) and
+ *                        one work group per other unit; every input read
+ *                        once.
  * Any output pointer may be NULL.  Results do not depend on the form.
  * Errors: GQ_ERR_INVALID (dt, in_mul, NULL table), GQ_ERR_DEVICE,
  * GQ_ERR_HIP (the occupancy query failed, e.g. no device).
  */
+#define GQ_FORM_PERSISTENT 0
+#define GQ_FORM_TWO_PASS 1
+#define GQ_FORM_SHORT_UNITS 2
 gq_status gq_units_launch_plan(const gq_units *u, gq_dtype dt, float in_mul, int64_t *q_groups,
-                               int32_t *q_one_launch, int64_t *r_groups, int32_t *r_one_launch);
+                               int32_t *q_form, int64_t *r_groups, int32_t *r_form);
 
 /*
  * gq_units_faults -- number of bounded waits that gave up on the table

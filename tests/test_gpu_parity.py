@@ -223,9 +223,10 @@ def test_unit_of_exactly_the_resident_grid(gq, oracle):
     assert gq.gq_units_schedule(units, gq.GQ_F32) == gq.GQ_SCHED_LAYER
     assert gq.gq_units_reduce_tile(units) == 16384
     plan = gq.gq_units_launch_plan(units, gq.GQ_F32, 1.0)
-    assert plan["q_groups"] == G and plan["q_one_launch"] and plan["r_one_launch"]
+    assert plan["q_groups"] == G
+    assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_PERSISTENT
     over = gq.gq_units_create(np.array([0, (G + 1) * 16384], dtype=np.int64))
-    assert not gq.gq_units_launch_plan(over, gq.GQ_F32, 1.0)["q_one_launch"]
+    assert gq.gq_units_launch_plan(over, gq.GQ_F32, 1.0)["q_form"] == gq.GQ_FORM_TWO_PASS
     xs = [_grad(rng, n, F32) for _ in range(2)]
     _run_and_compare(gq, oracle, xs, F32, off, 1.0, "resident_grid_unit", modes=("fused",))
 
@@ -507,3 +508,27 @@ def test_random_tables_sweep(gq, oracle):
                         q_out=want["q_out"][s0:])
         compare_step(got, want, W, check_r=True, label="sweep%d" % c)
     assert len(seen) == 4, seen
+
+
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("W", [3, 16])
+def test_short_unit_tables(gq, oracle, kind, W):
+    """Tables of many short tensors (every unit fits one tile, units of one
+    wave's share hold most elements) take the wait-free short-unit form in
+    both stages: one wave per (rank, unit), a work group per other unit.
+    Units of 1 .. 4096 elements at every offset, some spanning one slot more
+    than a wave's share (single tiles), some all zero."""
+    rng = np.random.default_rng(600 + W + 10 * kind)
+    lens = list(rng.integers(1, 4097, 900)) + [4096, 4095, 4097, 8000, 2049, 1, 2] * 3
+    rng.shuffle(lens)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(W)]
+    for u in rng.choice(len(lens), 20, replace=False):   # zero units on every rank
+        for x in xs:
+            x[off[u]:off[u + 1]] = 0
+    units = gq.gq_units_create(off)
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    plan = gq.gq_units_launch_plan(units, kind, in_mul)
+    assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_SHORT_UNITS, plan
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "short_units_W%d_k%d" % (W, kind))

@@ -62,6 +62,9 @@ def test_workload_every_element(gq, oracle, cfg):
     compare_step(step.host(), want, w.W, check_r=False, label=w.name + "/bench")
     step.reduce(fused=True, with_r=True)
     compare_step(step.host(), want, w.W, check_r=True, label=w.name + "/with_r")
+    plan = gq.gq_units_launch_plan(step.units, _kind(w), w.in_mul)
+    form = gq.GQ_FORM_SHORT_UNITS if cfg == 5 else gq.GQ_FORM_PERSISTENT
+    assert plan["q_form"] == plan["r_form"] == form, plan
     if cfg == 5:
         # the class structure of the small-tensor set really hits the edge rules
         zero_units = np.flatnonzero(want["scale"][0] == 0)
@@ -90,6 +93,8 @@ def test_workload_every_element_large(gq, oracle, cfg):
     step = GpuStep(gq, off, w.W, kind, w.n)
     assert gq.gq_units_schedule(step.units, kind) == gq.GQ_SCHED_CHUNK
     assert gq.gq_units_reduce_tile(step.units) == 16384
+    plan = gq.gq_units_launch_plan(step.units, kind, w.in_mul)
+    assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_PERSISTENT, plan
     step.quantize(dx, w.in_mul)
     step.reduce(fused=True, with_r=False)          # the benchmark's launch shape
     torch.cuda.synchronize()
