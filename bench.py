@@ -491,30 +491,38 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # the timed region: exactly K steps; an event before and after each
-    # step's quantize launch gives that kernel's duration (the roofline) and
-    # the stage breakdown without extra passes
-    e_q0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    e_q1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # the stage breakdown and the kernels' durations (the roofline): K steps
+    # with an event before each launch and one after the last, on the
+    # kernels' own stream, right before the timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        ev[2 * k].record(stream)
+        gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=stream)
+        ev[2 * k + 1].record(stream)
+        gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
+    ev[2 * args.steps].record(stream)
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]))
+    r_ms = float(np.mean([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]))
+    step_ms = [ev[2 * k].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]
+    instrumented_ms = ev[0].elapsed_time(ev[2 * args.steps]) / args.steps
+
+    # the timed region: exactly K steps between two events, with nothing else
+    # on the stream (an event recorded between two launches delays the
+    # second by a few microseconds)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        e_q0[k].record(stream)
-        gq.gq_quantize(dx, units, scales, codes, in_mul=w.in_mul, stream=stream)
-        e_q1[k].record(stream)
-        gq.gq_reduce_requantize(codes, scales, units, s_out, q_out, stream=stream)
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    nxt = e_q0[1:] + [end]
-    q_ms = float(np.mean([e_q0[k].elapsed_time(e_q1[k]) for k in range(args.steps)]))
-    r_ms = float(np.mean([e_q1[k].elapsed_time(nxt[k]) for k in range(args.steps)]))
-    step_ms = [e_q0[k].elapsed_time(nxt[k]) for k in range(args.steps)]
     faults = gq.gq_units_faults(units)
     if faults:
         print("a bounded cross-group wait gave up %d times: results invalid" % faults,
@@ -567,6 +575,9 @@ def main():
         # bytes of its fp32 gradient: the compression of the INT8 AllReduce
         "wire_bytes_vs_fp32": round((w.n + 4 * U) / (4.0 * w.n), 5),
         "algorithmic_bytes_per_step": b_alg,
+        # per-step and per-stage times from K more steps with an event
+        # around every launch (the events add a few microseconds per step)
+        "instrumented_ms_per_step": round(instrumented_ms, 4),
         "step_ms_median": round(float(np.median(step_ms)), 4),
         "step_ms_min": round(float(np.min(step_ms)), 4),
         "stages_ms": {"quantize": round(q_ms, 4), "reduce_requantize": round(r_ms, 4)},
@@ -574,7 +585,8 @@ def main():
         "pipeline": pipeline,
         "adaptive_chunk": adaptive,
         "ab_fp32": ab,
-        # the quantize stage is one launch of the persistent quantize kernel
+        # the quantize stage's kernel (one persistent launch on the per-chunk
+        # and per-layer workloads), timed by the events around its launches
         "roofline": {"bound": "hbm", "kernel": qkernel,
                      "achieved": round(q_achieved, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(q_achieved / (HBM_PEAK / 1e9), 4),
