@@ -254,6 +254,10 @@ def test_product_sources_never_use_the_oracle():
     assert not hits, hits
 
 
+KERNEL_FILE = (r"traffic_(k_quantize_layer|k_quantize_chunk|k_quantize_small|k_reduce_coop_wide|"
+               r"k_reduce_coop|k_reduce_small)_(\w+)\.txt$")
+
+
 def test_bench_traffic_follows_the_kernel_source(monkeypatch):
     """The bench reports measured traffic only from a counter summary taken
     on the current kernel source; any other summary reads as unmeasured."""
@@ -262,7 +266,7 @@ def test_bench_traffic_follows_the_kernel_source(monkeypatch):
     assert names, "no counter summaries committed"
     current = bench.kernel_source_hash()
     for name in names:
-        kernel, workload = re.match(r"traffic_(k_quantize_layer|k_quantize_chunk|k_reduce_coop_wide|k_reduce_coop)_(\w+)\.txt$", name).groups()
+        kernel, workload = re.match(KERNEL_FILE, name).groups()
         text = open(os.path.join(bench.PROFILES, name)).read()
         taken_on = re.search(r"kernel_source_sha256_16 = (\w+)", text).group(1)
         got = bench.measured_traffic(kernel, workload)
@@ -273,7 +277,7 @@ def test_bench_traffic_follows_the_kernel_source(monkeypatch):
             assert got is None, name
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     for name in names:
-        kernel, workload = re.match(r"traffic_(k_quantize_layer|k_quantize_chunk|k_reduce_coop_wide|k_reduce_coop)_(\w+)\.txt$", name).groups()
+        kernel, workload = re.match(KERNEL_FILE, name).groups()
         assert bench.measured_traffic(kernel, workload) is None
     assert bench.measured_traffic("k_quantize_layer", "no_such_workload") is None
 
