@@ -192,33 +192,44 @@ def _current_device():
     return torch.cuda.current_device()
 
 
-def _need(name, t, numel, dtypes):
-    """Host-side guard, checked before anything is enqueued: a contiguous
-    tensor on the current HIP device, of one of `dtypes`, holding at least
-    numel elements (the library reads and writes exactly what the call's
-    sizes say, so a short or mistyped buffer would be overrun)."""
+def _why(name, t, numel, dtypes, dev):
+    """The error for a tensor that fails its guard (None if it passes)."""
     if not getattr(t, "is_cuda", False):
-        raise ValueError("%s must be a tensor on the HIP device" % name)
+        return ValueError("%s must be a tensor on the HIP device" % name)
     if t.dtype not in dtypes:
-        raise TypeError("%s must be of dtype %s, got %s"
-                        % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+        return TypeError("%s must be of dtype %s, got %s"
+                         % (name, " or ".join(str(d) for d in dtypes), t.dtype))
     if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+        return ValueError("%s must be contiguous" % name)
     if t.numel() < numel:
-        raise ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), numel))
-    if t.device.index != _current_device():
-        raise ValueError("%s is on device %s, the current device is %d"
-                         % (name, t.device, _current_device()))
+        return ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), numel))
+    if t.get_device() != dev:
+        return ValueError("%s is on device %d, the current device is %d"
+                          % (name, t.get_device(), dev))
+    return None
 
 
-def _need_list(name, ts, W, numel, dtypes):
-    """W tensors, each passing _need."""
+def _need(name, t, numel, dtypes, dev):
+    """Host-side guard, checked before anything is enqueued: a contiguous
+    tensor on the current HIP device `dev`, of one of `dtypes`, holding at
+    least numel elements (the library reads and writes exactly what the
+    call's sizes say, so a short or mistyped buffer would be overrun)."""
+    e = _why(name, t, numel, dtypes, dev)
+    if e is not None:
+        raise e
+
+
+def _need_list(name, ts, W, numel, dtypes, dev):
+    """W tensors, each passing _need (one short-circuit test per tensor; the
+    reason is worked out only for a tensor that fails it)."""
     if not isinstance(ts, (list, tuple)):
         raise TypeError("%s must be a list of tensors" % name)
     if len(ts) != W:
         raise ValueError("%s holds %d tensors for %d ranks" % (name, len(ts), W))
     for i, t in enumerate(ts):
-        _need("%s[%d]" % (name, i), t, numel, dtypes)
+        if not (getattr(t, "is_cuda", False) and t.dtype in dtypes and t.numel() >= numel
+                and t.is_contiguous() and t.get_device() == dev):
+            raise _why("%s[%d]" % (name, i), t, numel, dtypes, dev) or ValueError(name)
 
 
 def _ranks(name, xs):
@@ -230,17 +241,34 @@ def _ranks(name, xs):
     return len(xs)
 
 
-def _grads(xs, numel):
+_TORCH = {}
+
+
+def _dt():
+    """(float32, float16, int8, int32, uint32, int64, float64) torch dtypes."""
+    if not _TORCH:
+        import torch
+        _TORCH["f32"] = (torch.float32,)
+        _TORCH["f16"] = (torch.float16,)
+        _TORCH["grad"] = (torch.float32, torch.float16)
+        _TORCH["i8"] = (torch.int8,)
+        _TORCH["bits"] = (torch.int32, torch.uint32)
+        _TORCH["i64"] = (torch.int64,)
+        _TORCH["f64"] = (torch.float64,)
+    return _TORCH
+
+
+def _grads(xs, numel, dev):
     """Gradient inputs: 1 .. GQ_MAX_RANKS tensors of one element type
     (float32 or float16), each of at least numel elements; returns (W,
     dtype code)."""
-    import torch
+    T = _dt()
     W = _ranks("xs", xs)
     dt = getattr(xs[0], "dtype", None)
-    if dt not in (torch.float32, torch.float16):
+    if dt not in T["grad"]:
         raise TypeError("gradient elements must be float32 or float16, got %s" % dt)
-    _need_list("xs", xs, W, numel, (dt,))
-    return W, (GQ_F32 if dt == torch.float32 else GQ_F16)
+    _need_list("xs", xs, W, numel, (dt,), dev)
+    return W, (GQ_F32 if dt == T["f32"][0] else GQ_F16)
 
 
 def _table(units):
@@ -249,19 +277,18 @@ def _table(units):
     return units
 
 
-def _f32():
-    import torch
-    return (torch.float32,)
-
-
-def _i8():
-    import torch
-    return (torch.int8,)
+_PTR_ARRAYS = {}
 
 
 def _ptrs(tensors):
-    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
-    return ctypes.cast(arr, ctypes.c_void_p), arr
+    """A host array of the tensors' device addresses: (its address, the
+    array, which must stay alive until the call returns)."""
+    n = len(tensors)
+    t = _PTR_ARRAYS.get(n)
+    if t is None:
+        t = _PTR_ARRAYS[n] = ctypes.c_uint64 * n
+    arr = t(*[x.data_ptr() for x in tensors])
+    return ctypes.addressof(arr), arr
 
 
 def gq_plan_chunks(numel, elem_bytes, chunk_bytes=CHUNK_BYTES, align_bytes=ALIGN_BYTES):
@@ -352,9 +379,8 @@ def gq_units_faults_async(units, count_out, stream=None):
     int32/uint32 tensor of at least one element) on the stream, without
     synchronizing; nonzero after the stream's sync means the outputs since
     the count was last cleared are invalid."""
-    import torch
     _table(units)
-    _need("count_out", count_out, 1, (torch.int32, torch.uint32))
+    _need("count_out", count_out, 1, _dt()["bits"], _current_device())
     _check(lib.gq_units_faults_async(units.handle, count_out.data_ptr(), _stream(stream)))
 
 
@@ -387,10 +413,10 @@ def gq_units_force_timeout(units):
 def gq_absmax(xs, units, amax_bits, in_mul=1.0, stream=None):
     """amax_bits: int32/uint32 tensor of W*n_units (rank-major), overwritten
     with the bit patterns of max|x*in_mul| per unit."""
-    import torch
     _table(units)
-    W, dt = _grads(xs, units.n)
-    _need("amax_bits", amax_bits, W * units.n_units, (torch.int32, torch.uint32))
+    dev = _current_device()
+    W, dt = _grads(xs, units.n, dev)
+    _need("amax_bits", amax_bits, W * units.n_units, _dt()["bits"], dev)
     px, keep = _ptrs(xs)
     _check(lib.gq_absmax(px, W, dt, in_mul, units.handle, amax_bits.data_ptr(),
                          _stream(stream)))
@@ -399,13 +425,14 @@ def gq_absmax(xs, units, amax_bits, in_mul=1.0, stream=None):
 def gq_quantize(xs, units, scales, codes, in_mul=1.0, amax_bits=None, stream=None):
     """Per-unit scales (float32, n_units each) and int8 codes (n each) of W
     gradients xs."""
-    import torch
     _table(units)
-    W, dt = _grads(xs, units.n)
-    _need_list("scales", scales, W, units.n_units, _f32())
-    _need_list("codes", codes, W, units.n, _i8())
+    dev = _current_device()
+    T = _dt()
+    W, dt = _grads(xs, units.n, dev)
+    _need_list("scales", scales, W, units.n_units, T["f32"], dev)
+    _need_list("codes", codes, W, units.n, T["i8"], dev)
     if amax_bits is not None:
-        _need("amax_bits", amax_bits, W * units.n_units, (torch.int32, torch.uint32))
+        _need("amax_bits", amax_bits, W * units.n_units, T["bits"], dev)
     px, k1 = _ptrs(xs)
     ps, k2 = _ptrs(scales)
     pq, k3 = _ptrs(codes)
@@ -420,15 +447,16 @@ def gq_quantize_noalloc(xs, h_off, d_off, scales, codes, in_mul=1.0, stream=None
     values.  The library keeps the maxima in a fixed array of its own
     (W * n_units <= GQ_NOALLOC_MAX_MAXIMA), shared by every call on the
     device: calls on one device must be ordered."""
-    import torch
     off = np.ascontiguousarray(h_off, dtype=np.int64)
     if off.ndim != 1 or off.size < 2:
         raise ValueError("h_off must hold n_units + 1 >= 2 offsets")
     U = off.size - 1
-    W, dt = _grads(xs, int(off[-1]))
-    _need("d_off", d_off, U + 1, (torch.int64,))
-    _need_list("scales", scales, W, U, _f32())
-    _need_list("codes", codes, W, int(off[-1]), _i8())
+    dev = _current_device()
+    T = _dt()
+    W, dt = _grads(xs, int(off[-1]), dev)
+    _need("d_off", d_off, U + 1, T["i64"], dev)
+    _need_list("scales", scales, W, U, T["f32"], dev)
+    _need_list("codes", codes, W, int(off[-1]), T["i8"], dev)
     px, k1 = _ptrs(xs)
     ps, k2 = _ptrs(scales)
     pq, k3 = _ptrs(codes)
@@ -436,17 +464,19 @@ def gq_quantize_noalloc(xs, h_off, d_off, scales, codes, in_mul=1.0, stream=None
                                    ps, pq, _stream(stream)))
 
 
-def _reduce_inputs(codes, scales, units):
+def _reduce_inputs(codes, scales, units, dev):
     _table(units)
+    T = _dt()
     W = _ranks("codes", codes)
-    _need_list("codes", codes, W, units.n, _i8())
-    _need_list("scales", scales, W, units.n_units, _f32())
+    _need_list("codes", codes, W, units.n, T["i8"], dev)
+    _need_list("scales", scales, W, units.n_units, T["f32"], dev)
     return W
 
 
 def gq_reduce_dequant(codes, scales, units, r_out, stream=None):
-    W = _reduce_inputs(codes, scales, units)
-    _need("r_out", r_out, units.n, _f32())
+    dev = _current_device()
+    W = _reduce_inputs(codes, scales, units, dev)
+    _need("r_out", r_out, units.n, _dt()["f32"], dev)
     pq, k1 = _ptrs(codes)
     ps, k2 = _ptrs(scales)
     _check(lib.gq_reduce_dequant(pq, ps, W, units.handle, r_out.data_ptr(), _stream(stream)))
@@ -454,19 +484,23 @@ def gq_reduce_dequant(codes, scales, units, r_out, stream=None):
 
 def gq_requantize(r, units, scale_out, q_out, stream=None):
     _table(units)
-    _need("r", r, units.n, _f32())
-    _need("scale_out", scale_out, units.n_units, _f32())
-    _need("q_out", q_out, units.n, _i8())
+    dev = _current_device()
+    T = _dt()
+    _need("r", r, units.n, T["f32"], dev)
+    _need("scale_out", scale_out, units.n_units, T["f32"], dev)
+    _need("q_out", q_out, units.n, T["i8"], dev)
     _check(lib.gq_requantize(r.data_ptr(), units.handle, scale_out.data_ptr(),
                              q_out.data_ptr(), _stream(stream)))
 
 
 def gq_reduce_requantize(codes, scales, units, scale_out, q_out, r_out=None, stream=None):
-    W = _reduce_inputs(codes, scales, units)
-    _need("scale_out", scale_out, units.n_units, _f32())
-    _need("q_out", q_out, units.n, _i8())
+    dev = _current_device()
+    T = _dt()
+    W = _reduce_inputs(codes, scales, units, dev)
+    _need("scale_out", scale_out, units.n_units, T["f32"], dev)
+    _need("q_out", q_out, units.n, T["i8"], dev)
     if r_out is not None:
-        _need("r_out", r_out, units.n, _f32())
+        _need("r_out", r_out, units.n, T["f32"], dev)
     pq, k1 = _ptrs(codes)
     ps, k2 = _ptrs(scales)
     rp = r_out.data_ptr() if r_out is not None else None
@@ -478,9 +512,10 @@ def gq_sum_f32(xs, r_out, in_mul=1.0, mean=False, stream=None):
     """fp32 rank-order sum of the unquantized gradients xs (divided by W if
     mean) into r_out (float32, n)."""
     _ranks("xs", xs)
+    dev = _current_device()
     n = xs[0].numel()
-    W, dt = _grads(xs, n)
-    _need("r_out", r_out, n, _f32())
+    W, dt = _grads(xs, n, dev)
+    _need("r_out", r_out, n, _dt()["f32"], dev)
     px, keep = _ptrs(xs)
     _check(lib.gq_sum_f32(px, W, dt, in_mul, n, 1 if mean else 0, r_out.data_ptr(),
                           _stream(stream)))
@@ -490,12 +525,13 @@ def gq_error_report(q, scale, ref, units, stats_out, stream=None):
     """Per-unit binary64 error statistics of the INT8 result (q, scale)
     against ref; stats_out: float64 tensor of n_units * GQ_STATS, columns
     named by STATS."""
-    import torch
     _table(units)
-    _need("q", q, units.n, _i8())
-    _need("scale", scale, units.n_units, _f32())
-    _need("ref", ref, units.n, _f32())
-    _need("stats_out", stats_out, units.n_units * GQ_STATS, (torch.float64,))
+    dev = _current_device()
+    T = _dt()
+    _need("q", q, units.n, T["i8"], dev)
+    _need("scale", scale, units.n_units, T["f32"], dev)
+    _need("ref", ref, units.n, T["f32"], dev)
+    _need("stats_out", stats_out, units.n_units * GQ_STATS, T["f64"], dev)
     _check(lib.gq_error_report(q.data_ptr(), scale.data_ptr(), ref.data_ptr(), units.handle,
                                stats_out.data_ptr(), _stream(stream)))
 
@@ -560,12 +596,14 @@ def gq_pipe_step(pipe, xs, q_slots, scale_slots, scale_out, q_out, in_mul=1.0, s
     of 2*W tensors (slot s of rank w at index s*W + w)."""
     if not isinstance(pipe, Pipe) or not getattr(pipe, "handle", None):
         raise ValueError("pipe must be a live plan (gq_pipe_create)")
-    W, dt = _grads(xs, pipe.n)
+    dev = _current_device()
+    T = _dt()
+    W, dt = _grads(xs, pipe.n, dev)
     se, su = gq_pipe_slots(pipe)
-    _need_list("q_slots", q_slots, 2 * W, se, _i8())
-    _need_list("scale_slots", scale_slots, 2 * W, su, _f32())
-    _need("scale_out", scale_out, pipe.n_units, _f32())
-    _need("q_out", q_out, pipe.n, _i8())
+    _need_list("q_slots", q_slots, 2 * W, se, T["i8"], dev)
+    _need_list("scale_slots", scale_slots, 2 * W, su, T["f32"], dev)
+    _need("scale_out", scale_out, pipe.n_units, T["f32"], dev)
+    _need("q_out", q_out, pipe.n, T["i8"], dev)
     px, k1 = _ptrs(xs)
     pq, k2 = _ptrs(q_slots)
     ps, k3 = _ptrs(scale_slots)

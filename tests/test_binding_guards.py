@@ -44,6 +44,9 @@ class Fake:
     def data_ptr(self):
         return 0x10000
 
+    def get_device(self):
+        return self.device.index if self.is_cuda else -1
+
 
 @pytest.fixture()
 def env(monkeypatch):
