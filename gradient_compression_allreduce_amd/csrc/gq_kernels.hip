@@ -1142,7 +1142,9 @@ void k_reduce_coop_wide(const RArgs a) {
 // wave's unit is its only item (no unit waits for the one before it on the
 // same wave), and the reduce keeps eight ranks' codes in flight for units
 // of more than one slot per lane.
-constexpr int SMALL_BLOCK = 256;
+// Two waves per work group: a group leaves only when its slowest unit is
+// done, and the units of one group may differ in length a thousandfold.
+constexpr int SMALL_BLOCK = 128;
 
 template <typename TIn, bool MUL>
 __global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
