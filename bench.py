@@ -123,7 +123,7 @@ def stage_kernels(gq, units, kind, in_mul):
         qkernel = ("k_quantize_chunk" if gq.gq_units_schedule(units, dt) == gq.GQ_SCHED_CHUNK
                    else "k_quantize_layer")
     if plan["r_form"] == gq.GQ_FORM_SHORT_UNITS:
-        rkernel = "k_reduce_small"
+        rkernel = "k_reduce_pieces"
     elif plan["r_form"] == gq.GQ_FORM_TWO_PASS:
         rkernel = "k_reduce"
     else:

@@ -72,6 +72,64 @@ void build_tiles(const std::vector<int64_t> &off, int V, int64_t cap_slots,
     unit_first[U] = static_cast<int32_t>(tiles.size());
 }
 
+// The per-wave work of a short reduce table (see gq::Table::d_pieces): each
+// unit of at most PIECE_WAVES * PIECE_SLOTS slots cut into pieces of
+// PIECE_SLOTS slots from its first slot, the pieces packed PIECE_WAVES to a work group in unit
+// order with no unit split between groups; the other units keep their one
+// tile each (a short table has no multi-tile unit).
+void build_pieces(const std::vector<int64_t> &off, int V, const std::vector<gq::Tile> &tiles,
+                  const std::vector<int32_t> &unit_first, std::vector<gq::Tile> &pieces,
+                  std::vector<gq::Tile> &rest) {
+    constexpr int PW = gq::PIECE_WAVES;
+    constexpr int64_t PS = gq::PIECE_SLOTS;
+    const int64_t U = static_cast<int64_t>(off.size()) - 1;
+    const gq::Tile empty = {0, 0, -1, 0, 0, -1};
+    int fill = 0;  // pieces in the current group
+    for (int64_t u = 0; u < U; ++u) {
+        const int64_t a = off[u], b = off[u + 1];
+        const int64_t j0 = a / V, j1 = (b + V - 1) / V;
+        const int64_t k = (j1 - j0 + PS - 1) / PS;
+        if (k > PW) {
+            gq::Tile tl = tiles[unit_first[u]];
+            tl.first = static_cast<int32_t>(rest.size());
+            rest.push_back(tl);
+            continue;
+        }
+        if (fill + k > PW) {
+            for (; fill < PW; ++fill) pieces.push_back(empty);
+            fill = 0;
+        }
+        for (int64_t i = 0; i < k; ++i) {
+            const int64_t pb = (j0 + PS * i) * V, pe = (j0 + PS * (i + 1)) * V;
+            pieces.push_back({pb > a ? pb : a, pe < b ? pe : b, static_cast<int32_t>(u), fill,
+                              static_cast<int32_t>(k), -1});
+        }
+        fill += static_cast<int>(k);
+        if (fill == PW) fill = 0;
+    }
+    if (fill > 0)
+        for (; fill < PW; ++fill) pieces.push_back(empty);
+}
+
+// The per-wave work of a short quantize table: the units of at most
+// cap_slots slots, one entry each (first: its index in the list); the other
+// units keep their one tile each.
+void build_short_units(const std::vector<int64_t> &off, int V, int64_t cap_slots,
+                       const std::vector<gq::Tile> &tiles, const std::vector<int32_t> &unit_first,
+                       std::vector<gq::Tile> &work, std::vector<gq::Tile> &rest) {
+    const int64_t U = static_cast<int64_t>(off.size()) - 1;
+    for (int64_t u = 0; u < U; ++u) {
+        const int64_t a = off[u], b = off[u + 1];
+        if ((b + V - 1) / V - a / V <= cap_slots) {
+            work.push_back({a, b, static_cast<int32_t>(u), static_cast<int32_t>(work.size()), 1, -1});
+        } else {
+            gq::Tile tl = tiles[unit_first[u]];
+            tl.first = static_cast<int32_t>(rest.size());
+            rest.push_back(tl);
+        }
+    }
+}
+
 template <typename T>
 hipError_t upload(T **dst, const std::vector<T> &src) {
     *dst = nullptr;
@@ -92,6 +150,8 @@ void free_table(gq::Table &t) {
     if (t.d_ctl) (void)hipFree(t.d_ctl);
     if (t.d_res) (void)hipFree(t.d_res);
     if (t.d_cnt) (void)hipFree(t.d_cnt);
+    if (t.d_short) (void)hipFree(t.d_short);
+    if (t.d_rest) (void)hipFree(t.d_rest);
     t = gq::Table{};
 }
 
@@ -315,7 +375,16 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             for (const gq::Tile &x : small) in_small += x.end - x.begin;
             t.small_dominant = 2 * in_small > off[n_units] - off[0];
         }
-        e = upload(&t.d_tiles, tiles);
+        if (gq::short_table(t)) {
+            std::vector<gq::Tile> work, rest;
+            if (ti == gq::TAB_R) build_pieces(off, V, tiles, unit_first, work, rest);
+            else build_short_units(off, V, 64 * gq::SHORT_SLOTS_Q, tiles, unit_first, work, rest);
+            t.n_short = static_cast<int64_t>(work.size());
+            t.n_rest = static_cast<int64_t>(rest.size());
+            e = upload(&t.d_short, work);
+            if (e == hipSuccess) e = upload(&t.d_rest, rest);
+        }
+        if (e == hipSuccess) e = upload(&t.d_tiles, tiles);
         if (e == hipSuccess) e = upload(&t.d_multi, multi);
         if (e == hipSuccess) e = upload(&t.d_unit_first, unit_first);
         if (e == hipSuccess) e = upload(&t.d_small, small);

@@ -60,8 +60,21 @@ constexpr int R_SLOTS_WIDE = 2;
 // with narrow tiles double that span: their waves sum a unit in two halves.
 constexpr int SMALL_SLOTS_Q = 16;    // fp32: 4096 elements, fp16: 8192 elements
 constexpr int SMALL_SLOTS_R = 2;     // 2048 elements (4096 in two halves, narrow tables)
+// The short-table quantize kernel's waves hold one slot more per lane: a
+// unit of 64 * SMALL_SLOTS_Q * V elements then fits at any offset.
+constexpr int SHORT_SLOTS_Q = SMALL_SLOTS_Q + 1;
 
 constexpr int kSlotElems[TAB_COUNT] = {4, 8, 16};  // V of each table
+
+// Short reduce tables (see short_table) cut every unit of at most
+// PIECE_WAVES * PIECE_SLOTS slots into pieces of PIECE_SLOTS slots (one
+// slot per lane of a wave), and pack the pieces into work groups of
+// PIECE_WAVES waves so that no unit straddles two groups (a group's unused
+// waves get empty pieces).  The waves of one unit combine their maxima in
+// LDS.
+constexpr int PIECE_WAVES = 8;
+constexpr int PIECE_LANE_SLOTS = 1;
+constexpr int PIECE_SLOTS = 64 * PIECE_LANE_SLOTS;
 
 // Cross-work-group state of the persistent kernels: one published-max word
 // per tile and rank and one result word per multi-tile unit and rank (high
@@ -85,6 +98,18 @@ struct Table {
     Tile *d_big = nullptr;          // [n_big], unit order (first: index into d_big)
     int32_t big_max_count = 1;      // largest tile count of a unit in d_big
     bool small_dominant = false;    // small units hold most elements
+    // short tables only: the per-wave work list and the tiles of the units
+    // it leaves out (first: index into d_rest).  Quantize tables: the units
+    // of at most 64 * SHORT_SLOTS_Q slots, one entry each.  Reduce
+    // table: the pieces of the units of at most PIECE_WAVES * PIECE_SLOTS
+    // slots, PIECE_WAVES per work group (a piece: the unit's elements in its
+    // slot range; first = the wave of the group that holds the unit's first
+    // piece, count = the unit's pieces; an unused wave's piece has count 0;
+    // n_short is a multiple of PIECE_WAVES).
+    int64_t n_short = 0;
+    Tile *d_short = nullptr;
+    int64_t n_rest = 0;
+    Tile *d_rest = nullptr;
     int32_t *d_multi = nullptr;     // [n_multi] indices of multi tiles
     uint32_t *d_partial = nullptr;  // [GQ_MAX_RANKS][n_tiles] per-tile maxima
     int32_t *d_unit_first = nullptr;  // [n_units+1] first tile of each unit
@@ -108,6 +133,9 @@ inline bool table_ready(const Table &t, int64_t n_units) {
     if (t.n_small + t.n_big < 1 || (t.n_small > 0 && !t.d_small) || (t.n_big > 0 && !t.d_big))
         return false;
     if (t.n_multi_units > 0 && (!t.d_pub || !t.d_res || !t.d_cnt)) return false;
+    if (short_table(t) && (t.n_short + t.n_rest < 1 || (t.n_short > 0 && !t.d_short) ||
+                           (t.n_rest > 0 && !t.d_rest)))
+        return false;
     return t.block > 0 && t.slots > 0;
 }
 

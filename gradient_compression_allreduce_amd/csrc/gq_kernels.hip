@@ -879,9 +879,9 @@ __device__ __forceinline__ void requantize_tile(const Tile &t, const float (&acc
 // halves, the first half's sums parked meanwhile in this wave's 8 KiB of
 // LDS (slot group g of lane l at wpark[g * 64 + l]; each lane reads back
 // only its own), and both halves are requantized with the whole unit's
-// scale.  Multi-slot units load RGW ranks ahead (one in the persistent
-// kernels, whose registers are sized for whole tiles).
-template <int SR, bool HALVES, int RGW = 1>
+// scale.  Multi-slot units load one rank ahead (the persistent kernels'
+// registers are sized for whole tiles).
+template <int SR, bool HALVES>
 __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, float4 *wpark) {
     const Tile t = load_desc(a.small, item);
     float acc[SR][RV];
@@ -894,7 +894,7 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
             Tile th = t;
             if (h == 0) th.end = half_end;
             else th.begin = half_end;
-            reduce_tile<SR, 64, RGW>(a, th, acc);
+            reduce_tile<SR, 64, 1>(a, th, acc);
             if (a.r) store_sum<SR, 64>(th, acc, a.r);
             m = umax(m, acc_absmax<SR>(acc));
             if (h == 0) {
@@ -944,7 +944,7 @@ __device__ __forceinline__ void reduce_small_unit(const RArgs &a, int64_t item, 
         requantize_tile<1, 64>(t, acc1, quant_params(sc, true), a.q_out);
         return;
     }
-    reduce_tile<SR, 64, RGW>(a, t, acc);
+    reduce_tile<SR, 64, 1>(a, t, acc);
     if (a.r) store_sum<SR, 64>(t, acc, a.r);
     const uint32_t m = wave_max(acc_absmax<SR>(acc));
     const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
@@ -1134,16 +1134,18 @@ void k_reduce_coop_wide(const RArgs a) {
 }
 
 // Tables whose units all fit one tile and whose small units hold most of
-// the elements (many short tensors): the small units take one wave per
-// (rank, unit) item in a plain launch whose work groups never wait on each
-// other (the few other units take one work group per tile, k_quantize or
-// k_reduce).  With no tile path beside them, these kernels need fewer
-// registers than the persistent ones, so more waves are resident, each
-// wave's unit is its only item (no unit waits for the one before it on the
-// same wave), and the reduce keeps eight ranks' codes in flight for units
-// of more than one slot per lane.
-// Two waves per work group: a group leaves only when its slowest unit is
-// done, and the units of one group may differ in length a thousandfold.
+// the elements (many short tensors) run both stages as plain launches whose
+// work groups never wait on each other: the quantize takes one wave per
+// (rank, unit) item for units of up to 64 * SHORT_SLOTS_Q slots
+// (k_quantize_small), the reduce one wave per piece of 64 slots
+// (k_reduce_pieces), and the few other units one work group per tile
+// (k_quantize, k_reduce).  With no tile path beside them, these kernels need
+// fewer registers than the persistent ones, so more waves are resident, and
+// each wave's work is its only item (none waits for the one before it on
+// the same wave).
+// Two waves per work group in the quantize: a group leaves only when its
+// slowest unit is done, and the units of one group may differ in length a
+// thousandfold.
 constexpr int SMALL_BLOCK = 128;
 
 template <typename TIn, bool MUL>
@@ -1151,17 +1153,36 @@ __global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
     const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (item >= static_cast<int64_t>(a.W) * a.n_small) return;
-    quantize_small_unit<TIn, SMALL_SLOTS_Q, MUL>(a, item);
+    quantize_small_unit<TIn, SHORT_SLOTS_Q, MUL>(a, item);
 }
 
-template <bool HALVES>
-__global__ __launch_bounds__(SMALL_BLOCK) void k_reduce_small(const RArgs a) {
-    __shared__ float4 spark[HALVES ? (SMALL_BLOCK / 64) * SMALL_SLOTS_R * (RV / 4) * 64 : 1];
-    float4 *wpark = spark + (HALVES ? (threadIdx.x >> 6) * (SMALL_SLOTS_R * (RV / 4) * 64) : 0);
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.n_small) return;
-    reduce_small_unit<SMALL_SLOTS_R, HALVES, 4>(a, item, wpark);
+// Short reduce tables: one wave per piece of PIECE_SLOTS slots (the ranks'
+// loads four at a time, eight in flight), the waves of a unit in one work
+// group.  Each wave's max goes through LDS to the unit's other waves, and
+// every wave requantizes its own piece with the unit's scale.  Against one
+// wave per unit (the unit summed in two halves of 128 slots, one parked in
+// LDS), a unit's slots are summed by several waves at once, with fewer
+// registers per wave.
+__global__ __launch_bounds__(PIECE_WAVES * 64) void k_reduce_pieces(const RArgs a) {
+    __shared__ uint32_t wmax[PIECE_WAVES];
+    const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const Tile p = load_desc(a.small, static_cast<int64_t>(blockIdx.x) * PIECE_WAVES + v);
+    constexpr int PS = PIECE_LANE_SLOTS;
+    float acc[PS][RV];
+    uint32_t m = 0;
+    if (p.count > 0) {
+        reduce_tile<PS, 64, 4>(a, p, acc);
+        if (a.r) store_sum<PS, 64>(p, acc, a.r);
+        m = wave_max(acc_absmax<PS>(acc));
+    }
+    if ((threadIdx.x & 63) == 0) wmax[v] = m;
+    __syncthreads();
+    if (p.count == 0) return;
+    uint32_t um = 0;
+    for (int i = 0; i < p.count; ++i) um = umax(um, wmax[p.first + i]);
+    const float sc = __fdiv_rn(__uint_as_float(um), 127.0f);
+    if (v == p.first && (threadIdx.x & 63) == 0) a.scale_out[p.unit] = sc;
+    requantize_tile<PS, 64>(p, acc, quant_params(sc, true), a.q_out);
 }
 
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
@@ -1272,18 +1293,21 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
     }
     if (short_table(t)) {
         // many short tensors: no exchange needed (see k_quantize_small)
-        if (t.n_small > 0) {
-            const int64_t items = static_cast<int64_t>(a.W) * t.n_small;
+        if (t.n_short > 0) {
+            QArgs c = a;
+            c.small = t.d_short;
+            c.n_small = t.n_short;
+            const int64_t items = static_cast<int64_t>(a.W) * t.n_short;
             hipLaunchKernelGGL((k_quantize_small<TIn, MUL>),
                                dim3(static_cast<unsigned>((items + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64))),
-                               dim3(SMALL_BLOCK), 0, s, a);
+                               dim3(SMALL_BLOCK), 0, s, c);
         }
-        if (t.n_big > 0) {
+        if (t.n_rest > 0) {
             QArgs c = a;
-            c.tiles = t.d_big;
-            c.n_tiles = t.n_big;
+            c.tiles = t.d_rest;
+            c.n_tiles = t.n_rest;
             hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_FUSED>),
-                               dim3(static_cast<unsigned>(t.n_big), static_cast<unsigned>(a.W)), block, 0, s, c);
+                               dim3(static_cast<unsigned>(t.n_rest), static_cast<unsigned>(a.W)), block, 0, s, c);
         }
         return hipGetLastError();
     }
@@ -1383,20 +1407,19 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
         return hipGetLastError();
     }
     if (requantize && short_table(t)) {
-        // many short tensors: no exchange needed (see k_reduce_small)
-        if (t.n_small > 0) {
+        // many short tensors: no exchange needed (see k_reduce_pieces)
+        if (t.n_short > 0) {
             RArgs c = a;
-            c.small = t.d_small;
-            c.n_small = t.n_small;
-            const unsigned groups = static_cast<unsigned>((t.n_small + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64));
-            if (S == R_SLOTS_NARROW) hipLaunchKernelGGL(k_reduce_small<true>, dim3(groups), dim3(SMALL_BLOCK), 0, s, c);
-            else hipLaunchKernelGGL(k_reduce_small<false>, dim3(groups), dim3(SMALL_BLOCK), 0, s, c);
+            c.small = t.d_short;
+            c.n_small = t.n_short;
+            hipLaunchKernelGGL(k_reduce_pieces, dim3(static_cast<unsigned>(t.n_short / PIECE_WAVES)),
+                               dim3(PIECE_WAVES * 64), 0, s, c);
         }
-        if (t.n_big > 0) {
+        if (t.n_rest > 0) {
             RArgs c = a;
-            c.tiles = t.d_big;
-            c.n_tiles = t.n_big;
-            hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_big)), block, 0, s, c);
+            c.tiles = t.d_rest;
+            c.n_tiles = t.n_rest;
+            hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_rest)), block, 0, s, c);
         }
         return hipGetLastError();
     }

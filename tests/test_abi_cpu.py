@@ -255,7 +255,7 @@ def test_product_sources_never_use_the_oracle():
 
 
 KERNEL_FILE = (r"traffic_(k_quantize_layer|k_quantize_chunk|k_quantize_small|k_reduce_coop_wide|"
-               r"k_reduce_coop|k_reduce_small)_(\w+)\.txt$")
+               r"k_reduce_coop|k_reduce_pieces)_(\w+)\.txt$")
 
 
 def test_bench_traffic_follows_the_kernel_source(monkeypatch):

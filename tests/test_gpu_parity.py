@@ -511,15 +511,24 @@ def test_random_tables_sweep(gq, oracle):
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
-@pytest.mark.parametrize("W", [3, 16])
-def test_short_unit_tables(gq, oracle, kind, W):
+@pytest.mark.parametrize("W,wide", [(3, False), (16, False), (5, True)])
+def test_short_unit_tables(gq, oracle, kind, W, wide):
     """Tables of many short tensors (every unit fits one tile, units of one
     wave's share hold most elements) take the wait-free short-unit form in
-    both stages: one wave per (rank, unit), a work group per other unit.
-    Units of 1 .. 4096 elements at every offset, some spanning one slot more
-    than a wave's share (single tiles), some all zero."""
+    both stages: in the quantize one wave per (rank, unit) for units of up to
+    64 * 17 slots, a work group per other unit; in the reduce one wave per
+    64-slot piece of a unit of up to eight pieces, a work group per other
+    unit.  Units of 1 .. 4096 elements at every offset, some spanning one
+    slot more than 64 * 16, some of exactly eight pieces, some all zero;
+    with `wide`, also units of 9 .. 16 pieces (one wide reduce tile each)
+    and units above 64 * 17 quantize slots."""
     rng = np.random.default_rng(600 + W + 10 * kind)
-    lens = list(rng.integers(1, 4097, 900)) + [4096, 4095, 4097, 8000, 2049, 1, 2] * 3
+    lens = list(rng.integers(1, 2049 if wide else 4097, 900))
+    lens += [4096, 4095, 4097, 8000, 8176, 2049, 1, 2] * 3
+    if wide:
+        # most elements of the units above 2048 in units above 8192: wide
+        # reduce tiles, whose small units are those of at most 128 slots
+        lens += [8193, 12000, 16000, 9000, 15000, 8192, 8191] * 2
     rng.shuffle(lens)
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     n = int(off[-1])
