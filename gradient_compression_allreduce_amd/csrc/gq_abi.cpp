@@ -72,43 +72,66 @@ void build_tiles(const std::vector<int64_t> &off, int V, int64_t cap_slots,
     unit_first[U] = static_cast<int32_t>(tiles.size());
 }
 
-// The per-wave work of a short reduce table (see gq::Table::d_pieces): each
+// The per-wave work of a short reduce table (see gq::Table::d_short): each
 // unit of at most PIECE_WAVES * PIECE_SLOTS slots cut into pieces of
-// PIECE_SLOTS slots from its first slot, the pieces packed PIECE_WAVES to a work group in unit
-// order with no unit split between groups; the other units keep their one
-// tile each (a short table has no multi-tile unit).
+// PIECE_SLOTS slots from its first slot, and the units packed whole into
+// work groups of PIECE_WAVES pieces, best fit in decreasing order of piece
+// count (units are independent, so their order is free, and a work group
+// with idle waves would hold resident slots for nothing); the other units
+// keep their one tile each (a short table has no multi-tile unit).
 void build_pieces(const std::vector<int64_t> &off, int V, const std::vector<gq::Tile> &tiles,
                   const std::vector<int32_t> &unit_first, std::vector<gq::Tile> &pieces,
                   std::vector<gq::Tile> &rest) {
     constexpr int PW = gq::PIECE_WAVES;
     constexpr int64_t PS = gq::PIECE_SLOTS;
     const int64_t U = static_cast<int64_t>(off.size()) - 1;
-    const gq::Tile empty = {0, 0, -1, 0, 0, -1};
-    int fill = 0;  // pieces in the current group
+    auto count = [&](int64_t u) {
+        return (((off[u + 1] + V - 1) / V - off[u] / V) + PS - 1) / PS;
+    };
+    // units by piece count, most first (counting sort, unit order within)
+    std::vector<std::vector<int64_t>> by_k(PW + 1);
     for (int64_t u = 0; u < U; ++u) {
-        const int64_t a = off[u], b = off[u + 1];
-        const int64_t j0 = a / V, j1 = (b + V - 1) / V;
-        const int64_t k = (j1 - j0 + PS - 1) / PS;
+        const int64_t k = count(u);
         if (k > PW) {
             gq::Tile tl = tiles[unit_first[u]];
             tl.first = static_cast<int32_t>(rest.size());
             rest.push_back(tl);
-            continue;
+        } else {
+            by_k[k].push_back(u);
         }
-        if (fill + k > PW) {
-            for (; fill < PW; ++fill) pieces.push_back(empty);
-            fill = 0;
-        }
-        for (int64_t i = 0; i < k; ++i) {
-            const int64_t pb = (j0 + PS * i) * V, pe = (j0 + PS * (i + 1)) * V;
-            pieces.push_back({pb > a ? pb : a, pe < b ? pe : b, static_cast<int32_t>(u), fill,
-                              static_cast<int32_t>(k), -1});
-        }
-        fill += static_cast<int>(k);
-        if (fill == PW) fill = 0;
     }
-    if (fill > 0)
-        for (; fill < PW; ++fill) pieces.push_back(empty);
+    std::vector<std::vector<gq::Tile>> groups;
+    std::vector<std::vector<int64_t>> with_free(PW);  // groups by free waves (1 .. PW-1)
+    for (int k = PW; k >= 1; --k) {
+        for (const int64_t u : by_k[k]) {
+            int c = k;
+            while (c < PW && with_free[c].empty()) ++c;
+            int64_t g;
+            if (c < PW) {
+                g = with_free[c].back();
+                with_free[c].pop_back();
+            } else {
+                g = static_cast<int64_t>(groups.size());
+                groups.emplace_back();
+                c = PW;
+            }
+            std::vector<gq::Tile> &grp = groups[g];
+            const int32_t first = static_cast<int32_t>(grp.size());
+            const int64_t a = off[u], b = off[u + 1], j0 = a / V;
+            for (int i = 0; i < k; ++i) {
+                const int64_t pb = (j0 + PS * i) * V, pe = (j0 + PS * (i + 1)) * V;
+                grp.push_back({pb > a ? pb : a, pe < b ? pe : b, static_cast<int32_t>(u), first, k,
+                               -1});
+            }
+            if (c - k > 0) with_free[c - k].push_back(g);
+        }
+    }
+    const gq::Tile empty = {0, 0, -1, 0, 0, -1};
+    pieces.reserve(groups.size() * PW);
+    for (const std::vector<gq::Tile> &grp : groups) {
+        pieces.insert(pieces.end(), grp.begin(), grp.end());
+        for (size_t i = grp.size(); i < static_cast<size_t>(PW); ++i) pieces.push_back(empty);
+    }
 }
 
 // The per-wave work of a short quantize table: the units of at most
