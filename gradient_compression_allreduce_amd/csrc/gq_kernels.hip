@@ -84,9 +84,19 @@ __device__ __forceinline__ uint4 fix_slot(const void *x, int64_t j, int64_t j1, 
     return load_slot16(x, j, b, e, n, 16 / In<TIn>::V);
 }
 
+// Rows of BLOCK slots that tile t covers (uniform over the work group).
+template <typename TIn, int BLOCK>
+__device__ __forceinline__ int tile_rows(const Tile &t) {
+    constexpr int V = In<TIn>::V;
+    const int64_t j0 = t.begin / V, j1 = (t.end + V - 1) / V;
+    return __builtin_amdgcn_readfirstlane(static_cast<int>((j1 - j0 + BLOCK - 1) / BLOCK));
+}
+
 // Issue the loads of the S slots of tile t, at indices clamped into the
 // buffer and without branches, so that all S loads are in flight together.
-template <typename TIn, int S, int BLOCK>
+// With ROWS (tiles often much shorter than S rows, such as the short units
+// that one wave takes), rows past the tile are not loaded.
+template <typename TIn, int S, int BLOCK, bool ROWS = false>
 __device__ __forceinline__ void issue_tile(const void *x, const Tile &t, int64_t n,
                                            typename In<TIn>::Raw (&raw)[S]) {
     constexpr int V = In<TIn>::V;
@@ -97,18 +107,20 @@ __device__ __forceinline__ void issue_tile(const void *x, const Tile &t, int64_t
     // whole slot (lanes past the tile all load that one address, which the
     // memory pipeline merges)
     const int64_t jmax = (j1 < nfull ? j1 : nfull) - 1;
+    const int rows = ROWS ? tile_rows<TIn, BLOCK>(t) : S;
     const uint4 *xv = static_cast<const uint4 *>(x);
     if (jmax >= 0) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-            raw[s] = load_stream(xv + (j < jmax ? j : jmax));
+            if (!ROWS || s < rows) raw[s] = load_stream(xv + (j < jmax ? j : jmax));
         }
     }
 }
 
-// Redo the few slots that are not whole slots inside the tile, and return
-// the max |x| bits of the tile.
+// Redo the few slots that are not whole slots inside the tile (slots past
+// the tile, loaded or not, become zero), and return the max |x| bits of the
+// tile.
 template <typename TIn, int S, int BLOCK>
 __device__ __forceinline__ uint32_t fix_tile(const void *x, const Tile &t, int64_t n,
                                              typename In<TIn>::Raw (&raw)[S]) {
@@ -127,10 +139,10 @@ __device__ __forceinline__ uint32_t fix_tile(const void *x, const Tile &t, int64
     return m;
 }
 
-template <typename TIn, int S, int BLOCK>
+template <typename TIn, int S, int BLOCK, bool ROWS = false>
 __device__ __forceinline__ uint32_t load_tile(const void *x, const Tile &t, int64_t n,
                                               typename In<TIn>::Raw (&raw)[S]) {
-    issue_tile<TIn, S, BLOCK>(x, t, n, raw);
+    issue_tile<TIn, S, BLOCK, ROWS>(x, t, n, raw);
     return fix_tile<TIn, S, BLOCK>(x, t, n, raw);
 }
 
@@ -349,7 +361,7 @@ __device__ __forceinline__ void quantize_small_unit(const QArgs &a, int64_t item
     const int w = static_cast<int>(item / a.n_small);
     const Tile t = load_desc(a.small, item - static_cast<int64_t>(w) * a.n_small);
     Raw raw[SS];
-    const uint32_t m = wave_max(load_tile<TIn, SS, 64>(a.x[w], t, a.n, raw));
+    const uint32_t m = wave_max(load_tile<TIn, SS, 64, true>(a.x[w], t, a.n, raw));
     const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
     if ((threadIdx.x & 63) == 0) a.scale[w][t.unit] = sc;
     quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
