@@ -824,15 +824,67 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         return fail(GQ_ERR_DEVICE, op, "current device %d, plan lives on device %d", dev, p->device);
     const hipStream_t s_main = static_cast<hipStream_t>(stream);
     const bool serial = p->mode == GQ_PIPE_SERIAL;
-    const hipStream_t s_red = serial ? s_main : p->aux;
     const int64_t esz = dt == GQ_F32 ? 4 : 2;
-    for (int64_t b = 0; b < p->n_buckets; ++b) {
+    const bool mul = in_mul != 1.0f;
+    const int64_t B = p->n_buckets;
+    auto tq = [&](int64_t b) -> const gq::Table & {
+        return p->tab[static_cast<size_t>(b)]->tab[q_table(dt)];
+    };
+    auto tr = [&](int64_t b) -> const gq::Table & {
+        return p->tab[static_cast<size_t>(b)]->tab[gq::TAB_R];
+    };
+    // Overlap schedules.  Kernels of two buckets run side by side, so their
+    // forms must not strand each other's work groups:
+    //  ALTERNATE  buckets alternate between the two streams, each bucket's
+    //             reduce right after its quantize on the same stream (code
+    //             slot b % 2 is then always used by one stream, and no event
+    //             orders the streams inside the step).  Any kernel of one
+    //             stream may run beside any kernel of the other, so every
+    //             kernel that waits on its own work groups gets a grid of at
+    //             most the compute unit count; this needs each such kernel
+    //             to fit at least two work groups per compute unit (one of
+    //             each of two such kernels then fits in any compute unit
+    //             that holds fewer than two, and together they never exceed
+    //             what the device holds at once).  A kernel that never
+    //             waits always finishes and frees its compute units.
+    //  EVENTS     otherwise: quantize on the caller's stream, reduce on the
+    //             second stream after an event, so that only bucket b's
+    //             reduce and bucket b+1's quantize meet; per such pair, both
+    //             run in their full forms if one of them never waits, and
+    //             else the reduce takes its form that never waits.
+    const int64_t cus = serial ? 0 : gq::device_cus();
+    if (!serial && cus < 1) return fail(GQ_ERR_HIP, op, "device query failed");
+    bool alternate = !serial;
+    for (int64_t b = 0; b < B && alternate; ++b) {
+        if (gq::quantize_waits(dt, mul, tq(b), 0) && gq::quantize_resident(dt, mul, tq(b)) < 2 * cus)
+            alternate = false;
+        if (gq::reduce_waits(tr(b), 0) && gq::reduce_resident(tr(b)) < 2 * cus) alternate = false;
+    }
+    hipError_t e = hipSuccess;
+    if (alternate) {
+        // the second stream starts after the caller's stream's earlier work
+        e = hipEventRecord(p->ev_q[0], s_main);
+        if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_q[0], 0);
+        if (e != hipSuccess) return launch_status(op, e);
+    }
+    for (int64_t b = 0; b < B; ++b) {
         const int s = static_cast<int>(b & 1);
         const gq_units *t = p->tab[static_cast<size_t>(b)];
         const int64_t base = p->base[static_cast<size_t>(b)];
-        // quantize bucket b into slot s (once the reduce of bucket b-2 has
-        // released it)
-        if (!serial && b >= 2 && hipStreamWaitEvent(s_main, p->ev_r[s], 0) != hipSuccess)
+        const hipStream_t s_q = (alternate && s == 1) ? p->aux : s_main;
+        const hipStream_t s_r = serial ? s_main : alternate ? s_q : p->aux;
+        int64_t q_cap = 0, r_cap = 0;
+        bool r_wait_free = false;
+        if (alternate) {
+            q_cap = gq::quantize_waits(dt, mul, tq(b), 0) ? cus : 0;
+            r_cap = gq::reduce_waits(tr(b), 0) ? cus : 0;
+        } else if (!serial && b + 1 < B) {
+            // EVENTS: this reduce meets the next bucket's quantize
+            r_wait_free = gq::quantize_waits(dt, mul, tq(b + 1), 0) && gq::reduce_waits(tr(b), 0);
+        }
+        // quantize bucket b into slot s (EVENTS: once the reduce of bucket
+        // b-2 has released it)
+        if (!serial && !alternate && b >= 2 && hipStreamWaitEvent(s_main, p->ev_r[s], 0) != hipSuccess)
             return fail(GQ_ERR_HIP, op, "hipStreamWaitEvent failed");
         gq::QArgs a = qa;
         for (int32_t w = 0; w < W; ++w) {
@@ -842,15 +894,13 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         }
         a.amax = nullptr;
         GQ_TRY(bind_qtable(op, t, dt, a));
-        hipError_t e = gq::launch_quantize(a, dt, t->tab[q_table(dt)], s_main);
-        if (!serial) {
+        e = gq::launch_quantize(a, dt, t->tab[q_table(dt)], s_q, q_cap);
+        if (!serial && !alternate) {
             if (e == hipSuccess) e = hipEventRecord(p->ev_q[s], s_main);
             if (e == hipSuccess) e = hipStreamWaitEvent(p->aux, p->ev_q[s], 0);
         }
         if (e != hipSuccess) return launch_status(op, e);
-        // reduce + requantize bucket b on the second stream, in the form
-        // whose work groups never wait on each other (it may share the
-        // device with the next bucket's quantize)
+        // reduce + requantize bucket b
         gq::RArgs r;
         GQ_TRY(fill_rargs(op, q_slot + s * W, scale_slot + s * W, W, r));
         r.r = nullptr;
@@ -858,12 +908,12 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
         r.n = t->n;
         r.scale_out = scale_out + p->u0[static_cast<size_t>(b)];
         r.q_out = q_out + base;
-        e = gq::launch_reduce(r, t->tab[gq::TAB_R], true, !serial, s_red);
-        if (!serial && e == hipSuccess) e = hipEventRecord(p->ev_r[s], p->aux);
+        e = gq::launch_reduce(r, t->tab[gq::TAB_R], true, r_wait_free, s_r, r_cap);
+        if (!serial && !alternate && e == hipSuccess) e = hipEventRecord(p->ev_r[s], p->aux);
         if (e != hipSuccess) return launch_status(op, e);
     }
     if (serial) return ok();
-    hipError_t e = hipEventRecord(p->ev_done, p->aux);
+    e = hipEventRecord(p->ev_done, p->aux);
     if (e == hipSuccess) e = hipStreamWaitEvent(s_main, p->ev_done, 0);
     return launch_status(op, e);
 }

@@ -229,12 +229,15 @@ struct EArgs {
 // Launchers (gq_kernels.hip, gq_check.hip).  Each returns the first launch
 // error.
 hipError_t launch_absmax(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
-hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s);
+// cap > 0 limits the persistent kernel's grid to cap work groups (the
+// one-launch form then runs only if no unit spans more tiles than that).
+hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s,
+                           int64_t cap = 0);
 // wait_free: never use the persistent kernel (whose work groups wait on
 // each other); used where another kernel may hold the device's compute
 // units at the same time.
 hipError_t launch_reduce(const RArgs &a, const Table &t, bool requantize, bool wait_free,
-                         hipStream_t s);
+                         hipStream_t s, int64_t cap = 0);
 hipError_t launch_sum_f32(const SArgs &a, gq_dtype dt, hipStream_t s);
 hipError_t launch_copy_word(const uint32_t *src, uint32_t *dst, hipStream_t s);
 
@@ -262,6 +265,13 @@ hipError_t launch_quantize_noalloc(const NoallocArgs &a, void *scratch_dev, hipS
 // one-launch form, which runs when no unit spans more tiles than this.
 int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t);
 int64_t reduce_resident(const Table &t);
+// The current device's compute units (0 if the query failed).
+int64_t device_cus();
+// Whether the fused stage of a table, launched with grid cap `cap` (0: none),
+// runs a kernel whose work groups wait on each other (the one-launch
+// persistent form on a table with a unit of several tiles).
+bool quantize_waits(gq_dtype dt, bool mul, const Table &t, int64_t cap);
+bool reduce_waits(const Table &t, int64_t cap);
 hipError_t launch_error_report(const EArgs &a, hipStream_t s);
 
 }  // namespace gq

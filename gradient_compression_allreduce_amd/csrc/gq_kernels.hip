@@ -1296,7 +1296,7 @@ constexpr auto coop_quantize_kernel() {
 }
 
 template <typename TIn, int BLOCK, bool MUL>
-hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
+hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s, int64_t cap) {
     const dim3 block(BLOCK);
     const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
     if (a.amax != nullptr) {
@@ -1324,7 +1324,8 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
         return hipGetLastError();
     }
     constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
-    const int64_t resident = resident_groups<coop>(BLOCK);
+    int64_t resident = resident_groups<coop>(BLOCK);
+    if (cap > 0 && cap < resident) resident = cap;
     if (resident >= t.big_max_count) {
         // one launch: the tiles of the other units through the ticket
         // counter, then the small units (one wave each)
@@ -1347,7 +1348,7 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s) {
 }
 
 template <typename TIn, bool MUL>
-hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
+hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s, int64_t cap) {
     QArgs a = a0;
     a.partial = t.d_partial;
     a.tiles = t.d_tiles;
@@ -1358,8 +1359,8 @@ hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s) {
     a.n_multi_units = t.n_multi_units;
     a.small = t.d_small;
     a.n_small = t.n_small;
-    if (t.block == Q_BLOCK_CHUNK) return quantize_geom<TIn, Q_BLOCK_CHUNK, MUL>(a, t, s);
-    return quantize_geom<TIn, Q_BLOCK_LAYER, MUL>(a, t, s);
+    if (t.block == Q_BLOCK_CHUNK) return quantize_geom<TIn, Q_BLOCK_CHUNK, MUL>(a, t, s, cap);
+    return quantize_geom<TIn, Q_BLOCK_LAYER, MUL>(a, t, s, cap);
 }
 
 template <typename TIn, int BLOCK>
@@ -1395,12 +1396,15 @@ hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s) {
+hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s,
+                           int64_t cap) {
     if (!table_ready(t, a.n_units)) return hipErrorInvalidValue;
     const bool mul = a.in_mul != 1.0f;
     if (dt == GQ_F32)
-        return mul ? quantize_typed<float, true>(a, t, s) : quantize_typed<float, false>(a, t, s);
-    return mul ? quantize_typed<__half, true>(a, t, s) : quantize_typed<__half, false>(a, t, s);
+        return mul ? quantize_typed<float, true>(a, t, s, cap)
+                   : quantize_typed<float, false>(a, t, s, cap);
+    return mul ? quantize_typed<__half, true>(a, t, s, cap)
+               : quantize_typed<__half, false>(a, t, s, cap);
 }
 
 template <int S>
@@ -1410,7 +1414,8 @@ constexpr auto coop_reduce_kernel() {
 }
 
 template <int S>
-hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free, hipStream_t s) {
+hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free, hipStream_t s,
+                       int64_t cap) {
     const dim3 block(R_BLOCK);
     if (!requantize) {
         a.list = nullptr;
@@ -1436,7 +1441,8 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
         return hipGetLastError();
     }
     constexpr auto coop = coop_reduce_kernel<S>();
-    const int64_t resident = resident_groups<coop>(R_BLOCK);
+    int64_t resident = resident_groups<coop>(R_BLOCK);
+    if (cap > 0 && cap < resident) resident = cap;
     if (!wait_free && resident >= t.big_max_count) {
         RArgs c = a;
         c.small = t.d_small;
@@ -1482,8 +1488,24 @@ int64_t reduce_resident(const Table &t) {
     return resident_groups<coop_reduce_kernel<R_SLOTS_NARROW>()>(R_BLOCK);
 }
 
+int64_t device_cus() { return device_info().cus; }
+
+bool quantize_waits(gq_dtype dt, bool mul, const Table &t, int64_t cap) {
+    if (short_table(t) || t.big_max_count <= 1) return false;
+    int64_t resident = quantize_resident(dt, mul, t);
+    if (cap > 0 && cap < resident) resident = cap;
+    return resident >= t.big_max_count;
+}
+
+bool reduce_waits(const Table &t, int64_t cap) {
+    if (short_table(t) || t.big_max_count <= 1) return false;
+    int64_t resident = reduce_resident(t);
+    if (cap > 0 && cap < resident) resident = cap;
+    return resident >= t.big_max_count;
+}
+
 hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,
-                         hipStream_t s) {
+                         hipStream_t s, int64_t cap) {
     if (!table_ready(t, 1)) return hipErrorInvalidValue;
     if (t.block != R_BLOCK || (t.slots != R_SLOTS_NARROW && t.slots != R_SLOTS_WIDE))
         return hipErrorInvalidValue;
@@ -1495,8 +1517,9 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool 
     a.res = t.d_res;
     a.cnt = t.d_cnt;
     a.ctl = t.d_ctl;
-    if (t.slots == R_SLOTS_WIDE) return reduce_geom<R_SLOTS_WIDE>(a, t, requantize, wait_free, s);
-    return reduce_geom<R_SLOTS_NARROW>(a, t, requantize, wait_free, s);
+    if (t.slots == R_SLOTS_WIDE)
+        return reduce_geom<R_SLOTS_WIDE>(a, t, requantize, wait_free, s, cap);
+    return reduce_geom<R_SLOTS_NARROW>(a, t, requantize, wait_free, s, cap);
 }
 
 }  // namespace gq

@@ -51,8 +51,11 @@
  *     Two of them side by side could each hold compute units the other
  *     needs; their waits then give up after about a second, the tables'
  *     fault counters (gq_units_faults) record it, and those calls' outputs
- *     are invalid.  gq_pipe_step's own two streams are safe: its reduce
- *     runs in a form that never waits.
+ *     are invalid.  gq_pipe_step's own two streams are safe: the kernels it
+ *     runs side by side either are both wholly resident at once (grids
+ *     capped at the compute unit count, two work groups per compute unit)
+ *     or include one that never waits, and otherwise its reduce takes a
+ *     form that never waits.
  *   - Non-finite inputs follow IEEE arithmetic (see above); there is no
  *     error for them.
  */
@@ -348,11 +351,18 @@ gq_status gq_reduce_requantize(const int8_t *const *q, const float *const *scale
  * the stages of successive gradient blocks with double buffering, and its
  * tuning parameters (§4.2) set the pipeline depth to 2.  Here the blocks
  * are buckets (consecutive groups of whole units, such as a data-parallel
- * job's 25 MiB gradient buckets): bucket b's quantize runs on the caller's
- * stream into code slot b % 2, and its reduce + requantize runs on a second
- * stream once that quantize is done, overlapping bucket b+1's quantize;
- * bucket b+2's quantize waits until bucket b's reduce has released the
- * slot.  Two slots of codes stand in for the whole model's codes. */
+ * job's 25 MiB gradient buckets), and two slots of codes stand in for the
+ * whole model's codes.  Bucket b uses code slot b % 2.  Where every kernel
+ * of the plan that waits on its own work groups fits two of them per
+ * compute unit, buckets alternate between the caller's stream and a second
+ * stream (even buckets on the caller's), each bucket's quantize then its
+ * reduce + requantize on its own stream, so that a bucket's stages overlap
+ * the other stream's bucket with no event inside the step; the waiting
+ * kernels' grids are then capped at the compute unit count (two of them
+ * side by side are both wholly resident).  Otherwise every quantize runs
+ * on the caller's stream and every reduce on the second stream after an
+ * event, bucket b's reduce overlapping bucket b+1's quantize, and bucket
+ * b+2's quantize waits until bucket b's reduce has released the slot. */
 
 typedef struct gq_pipe gq_pipe;
 
@@ -364,8 +374,8 @@ typedef struct gq_pipe gq_pipe;
  *               strictly increasing, bucket_units[n_buckets] = n_units.
  * mode          GQ_PIPE_OVERLAP: the two streams above.  GQ_PIPE_SERIAL:
  *               every stage on the caller's stream, bucket after bucket
- *               (no overlap; the reduce may then use its persistent form,
- *               and reads each bucket's codes soon after they were written).
+ *               (no overlap; every stage in its full form, each bucket's
+ *               codes read soon after they were written).
  * out           receives the plan.
  * Builds one unit table per bucket, a second stream (default priority) and
  * the events that order the two; allocates and synchronizes.  Errors:
