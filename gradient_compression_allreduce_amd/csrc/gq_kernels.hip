@@ -717,6 +717,17 @@ __global__ __launch_bounds__(BLOCK) void k_quantize(const QArgs a) {
 
 constexpr int RV = 16;  // codes per reduce slot
 
+// Rank w's scale of unit u, through the scalar cache (the same for every
+// lane of a work group).  A vector load here would join the code loads'
+// in-order completion count, so that waiting for the scale would also wait
+// for every code load issued before it (the ranks loaded ahead included).
+// The scales are inputs, written before the launch (the launch's acquire
+// makes them visible to the scalar cache) and never written by it.
+__device__ __forceinline__ float rank_scale(const RArgs &a, int w, int32_t u) {
+    using ConstF = __attribute__((address_space(4))) const float;
+    return ((ConstF *)(a.scale[w]))[u];
+}
+
 // acc += fl(q * sw) for the 16 codes of each held slot: each code is
 // converted from its signed byte (one instruction with a byte-select source
 // operand) and multiplied by sw with one rounding, then added.
@@ -745,61 +756,80 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
 #pragma unroll
         for (int k = 0; k < RV; ++k) acc[s][k] = 0.0f;
 
-    // Codes are loaded RG ranks at a time, the next group while the current
-    // one is accumulated.  Loads are issued at indices clamped into the
-    // buffer, without branches; slots past the tile or at the buffer's short
-    // end are redone afterwards.  Whole 16-byte slots are read even where a
-    // unit boundary cuts them (the bytes belong to the rank's buffer); sums
-    // of elements outside the tile are cleared below.
+    // Codes are loaded RG ranks at a time into two buffers in turn: the
+    // next group's loads are issued before the current group is
+    // accumulated, and no buffer is copied into the other (a copy would
+    // wait for the loads just issued).  Every load is issued on every path,
+    // and no loaded value is replaced on some lanes only (the merge would be
+    // a copy), so that the hardware's in-order load count tells each
+    // group's wait exactly; a rank past the last one loads the last rank's
+    // first slot again (one cache line, never used).  Loads are issued at
+    // indices clamped into the buffer, without branches.  Slots past the
+    // tile are summed from those clamped loads and their sums cleared below;
+    // a slot at the buffer's short end (n not a multiple of 16) is summed
+    // again afterwards from its bytes.  Whole 16-byte slots are read even
+    // where a unit boundary cuts them (the bytes belong to the rank's
+    // buffer); sums of elements outside the tile are cleared below.
     const int64_t nfull = a.n / RV;
     const int64_t jmax = (j1 < nfull ? j1 : nfull) - 1;
-    uint4 cur[RG][S], nxt[RG][S];
+    // slot jb + o, o = min(lane's slot - jb, jmax - jb), jb = min(j0, jmax)
+    const int64_t jb = j0 < jmax ? j0 : jmax;
+    const uint32_t lim = static_cast<uint32_t>(jmax - jb);
+    const uint32_t o0 = static_cast<uint32_t>(j0 - jb) + static_cast<uint32_t>(tid);
+    uint4 bufA[RG][S], bufB[RG][S];
     auto issue = [&](int w0, uint4 (&v)[RG][S]) {
         if (jmax < 0) return;
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
-            if (w0 + r >= a.W) break;
+            const bool past = w0 + r >= a.W;
+            const int w = past ? a.W - 1 : w0 + r;
             if constexpr (OFF32) {
-                // slot jb + o, o = min(lane's slot - jb, jmax - jb): the same
-                // clamped slot as below (jb = min(j0, jmax))
-                const int64_t jb = j0 < jmax ? j0 : jmax;
-                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]) + jb;
-                const uint32_t lim = static_cast<uint32_t>(jmax - jb);
-                const uint32_t o0 = static_cast<uint32_t>(j0 - jb) + static_cast<uint32_t>(tid);
+                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w]) + jb;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const uint32_t o = o0 + static_cast<uint32_t>(s * BLOCK);
-                    v[r][s] = load_stream(qv + (o < lim ? o : lim));
+                    v[r][s] = load_stream(qv + (past ? 0u : (o < lim ? o : lim)));
                 }
             } else {
-                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w0 + r]);
+                const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w]);
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-                    v[r][s] = load_stream(qv + (j < jmax ? j : jmax));
+                    v[r][s] = load_stream(qv + (past ? jb : (j < jmax ? j : jmax)));
                 }
             }
         }
     };
-    issue(0, cur);
-    for (int w0 = 0; w0 < a.W; w0 += RG) {
-        if (w0 + RG < a.W) issue(w0 + RG, nxt);
+    auto consume = [&](int w0, uint4 (&v)[RG][S]) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const int w = w0 + r;
             if (w >= a.W) break;
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
-                if (!(j < j1 && j < nfull))
-                    cur[r][s] = (j < j1) ? load_tail16(a.q[w], j * RV, a.n) : make_uint4(0, 0, 0, 0);
-            }
-            accumulate<S>(cur[r], a.scale[w][t.unit], acc);
+            accumulate<S>(v[r], rank_scale(a, w, t.unit), acc);
         }
+    };
+    issue(0, bufA);
+    for (int w0 = 0; w0 < a.W; w0 += 2 * RG) {
+        issue(w0 + RG, bufB);
+        consume(w0, bufA);
+        issue(w0 + 2 * RG, bufA);
+        consume(w0 + RG, bufB);
+    }
+    // the buffer's short last slot, from its bytes, in rank order
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
+    for (int s = 0; s < S; ++s) {
+        const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
+        if (j < j1 && j >= nfull) {
+            float part[1][RV];
 #pragma unroll
-            for (int s = 0; s < S; ++s) cur[r][s] = nxt[r][s];
+            for (int k = 0; k < RV; ++k) part[0][k] = 0.0f;
+            for (int w = 0; w < a.W; ++w) {
+                const uint4 c[1] = {load_tail16(a.q[w], j * RV, a.n)};
+                accumulate<1>(c, rank_scale(a, w, t.unit), part);
+            }
+#pragma unroll
+            for (int k = 0; k < RV; ++k) acc[s][k] = part[0][k];
+        }
     }
     // elements outside the tile never reach a max or a store (0 * inf = NaN)
 #pragma unroll
@@ -1168,8 +1198,69 @@ __global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
     quantize_small_unit<TIn, SHORT_SLOTS_Q, MUL>(a, item);
 }
 
-// Short reduce tables: one wave per piece of PIECE_SLOTS slots (the ranks'
-// loads four at a time, eight in flight), the waves of a unit in one work
+// Rank-order dequant-accumulate of one wave's piece (at most 64 slots, one
+// per lane), eight ranks at a time: the eight ranks' code pointers are read
+// together (one scalar load), then all eight ranks' loads are issued, each
+// lane addressing its slot by a 32-bit offset from the piece's first slot,
+// before any is accumulated.  As in reduce_tile, a slot at the buffer's
+// short end is summed again from its bytes, and sums of elements outside
+// the piece are cleared.
+__device__ __forceinline__ void reduce_piece(const RArgs &a, const Tile &t, float (&acc)[1][RV]) {
+    const int64_t lane = opaque_tid<64>();
+    const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
+#pragma unroll
+    for (int k = 0; k < RV; ++k) acc[0][k] = 0.0f;
+    const int64_t nfull = a.n / RV;
+    const int64_t jmax = (j1 < nfull ? j1 : nfull) - 1;
+    const int64_t j = j0 + lane;
+    // slot jb + o, o = min(j - jb, jmax - jb), jb = min(j0, jmax)
+    const int64_t jb = j0 < jmax ? j0 : jmax;
+    const uint32_t lim = static_cast<uint32_t>(jmax - jb);
+    const uint32_t o = static_cast<uint32_t>(j - jb) < lim ? static_cast<uint32_t>(j - jb) : lim;
+    for (int w0 = 0; w0 < a.W; w0 += 8) {
+        const int nr = a.W - w0 < 8 ? a.W - w0 : 8;
+        // past the last rank, rank w0's slot again (loaded, never used): the
+        // loads stay unconditional, so none waits for the ones before it
+        const int8_t *qp[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int8_t *q = a.q[w0 + r];  // w0 + 8 <= GQ_MAX_RANKS
+            qp[r] = r < nr ? q : a.q[w0];
+        }
+        uint4 v[8];
+        if (jmax >= 0) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                v[r] = load_stream(reinterpret_cast<const uint4 *>(qp[r]) + jb + o);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (r >= nr) break;
+            const uint4 c[1] = {v[r]};
+            accumulate<1>(c, rank_scale(a, w0 + r, t.unit), acc);
+        }
+    }
+    if (j < j1 && j >= nfull) {
+        // the buffer's short last slot, from its bytes, in rank order
+#pragma unroll
+        for (int k = 0; k < RV; ++k) acc[0][k] = 0.0f;
+        for (int w = 0; w < a.W; ++w) {
+            const uint4 c[1] = {load_tail16(a.q[w], j * RV, a.n)};
+            accumulate<1>(c, rank_scale(a, w, t.unit), acc);
+        }
+    }
+    const int64_t i0 = j * RV;
+    if (!(j < j1 && i0 >= t.begin && i0 + RV <= t.end)) {
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+            const int64_t i = i0 + k;
+            if (!(j < j1 && i >= t.begin && i < t.end)) acc[0][k] = 0.0f;
+        }
+    }
+}
+
+// Short reduce tables: one wave per piece of PIECE_SLOTS slots (eight
+// ranks' loads in flight, reduce_piece), the waves of a unit in one work
 // group.  Each wave's max goes through LDS to the unit's other waves, and
 // every wave requantizes its own piece with the unit's scale.  Against one
 // wave per unit (the unit summed in two halves of 128 slots, one parked in
@@ -1180,10 +1271,11 @@ __global__ __launch_bounds__(PIECE_WAVES * 64) void k_reduce_pieces(const RArgs 
     const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Tile p = load_desc(a.small, static_cast<int64_t>(blockIdx.x) * PIECE_WAVES + v);
     constexpr int PS = PIECE_LANE_SLOTS;
+    static_assert(PS == 1, "reduce_piece takes one slot per lane");
     float acc[PS][RV];
     uint32_t m = 0;
     if (p.count > 0) {
-        reduce_tile<PS, 64, 4>(a, p, acc);
+        reduce_piece(a, p, acc);
         if (a.r) store_sum<PS, 64>(p, acc, a.r);
         m = wave_max(acc_absmax<PS>(acc));
     }
