@@ -778,7 +778,6 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
     const uint32_t o0 = static_cast<uint32_t>(j0 - jb) + static_cast<uint32_t>(tid);
     uint4 bufA[RG][S], bufB[RG][S];
     auto issue = [&](int w0, uint4 (&v)[RG][S]) {
-        if (jmax < 0) return;
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const bool past = w0 + r >= a.W;
@@ -808,12 +807,14 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
             accumulate<S>(v[r], rank_scale(a, w, t.unit), acc);
         }
     };
-    issue(0, bufA);
-    for (int w0 = 0; w0 < a.W; w0 += 2 * RG) {
-        issue(w0 + RG, bufB);
-        consume(w0, bufA);
-        issue(w0 + 2 * RG, bufA);
-        consume(w0 + RG, bufB);
+    if (jmax >= 0) {  // (else the buffer is one short slot, summed below)
+        issue(0, bufA);
+        for (int w0 = 0; w0 < a.W; w0 += 2 * RG) {
+            issue(w0 + RG, bufB);
+            consume(w0, bufA);
+            issue(w0 + 2 * RG, bufA);
+            consume(w0 + RG, bufB);
+        }
     }
     // the buffer's short last slot, from its bytes, in rank order
 #pragma unroll
