@@ -747,8 +747,11 @@ __device__ __forceinline__ void accumulate(const uint4 (&v)[S], float sw, float 
 // Rank-order dequant-accumulate of the S slots of tile t into acc.  With
 // OFF32, a lane's loads are addressed from the tile's first slot by a 32-bit
 // offset (a tile spans at most S * BLOCK slots), which saves registers.
-template <int S, int BLOCK, int RG = 4, bool OFF32 = false>
+// WT > 0: the rank count is WT (= a.W), known when compiling, and the rank
+// loop unrolls fully (no loop-carried buffers for the compiler to copy).
+template <int S, int BLOCK, int RG = 4, bool OFF32 = false, int WT = 0>
 __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float (&acc)[S][RV]) {
+    const int W = WT > 0 ? WT : a.W;
     const int64_t tid = opaque_tid<BLOCK>();
     const int64_t j0 = t.begin / RV, j1 = (t.end + RV - 1) / RV;
 #pragma unroll
@@ -780,8 +783,8 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
     auto issue = [&](int w0, uint4 (&v)[RG][S]) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
-            const bool past = w0 + r >= a.W;
-            const int w = past ? a.W - 1 : w0 + r;
+            const bool past = w0 + r >= W;
+            const int w = past ? W - 1 : w0 + r;
             if constexpr (OFF32) {
                 const uint4 *qv = reinterpret_cast<const uint4 *>(a.q[w]) + jb;
 #pragma unroll
@@ -803,17 +806,27 @@ __device__ __forceinline__ void reduce_tile(const RArgs &a, const Tile &t, float
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const int w = w0 + r;
-            if (w >= a.W) break;
+            if (w >= W) break;
             accumulate<S>(v[r], rank_scale(a, w, t.unit), acc);
         }
     };
     if (jmax >= 0) {  // (else the buffer is one short slot, summed below)
         issue(0, bufA);
-        for (int w0 = 0; w0 < a.W; w0 += 2 * RG) {
-            issue(w0 + RG, bufB);
-            consume(w0, bufA);
-            issue(w0 + 2 * RG, bufA);
-            consume(w0 + RG, bufB);
+        if constexpr (WT > 0) {
+#pragma unroll
+            for (int w0 = 0; w0 < WT; w0 += 2 * RG) {
+                issue(w0 + RG, bufB);
+                consume(w0, bufA);
+                if (w0 + 2 * RG < WT) issue(w0 + 2 * RG, bufA);
+                consume(w0 + RG, bufB);
+            }
+        } else {
+            for (int w0 = 0; w0 < a.W; w0 += 2 * RG) {
+                issue(w0 + RG, bufB);
+                consume(w0, bufA);
+                issue(w0 + 2 * RG, bufA);
+                consume(w0 + RG, bufB);
+            }
         }
     }
     // the buffer's short last slot, from its bytes, in rank order
@@ -1080,7 +1093,9 @@ void k_reduce_coop(const RArgs a) {
 // stores and loads are free of bank conflicts) and reads back only its own,
 // so parking needs no barrier.  Two tiles of sums would not fit in
 // registers next to a tile's loads; in LDS they take 64 KiB per work group.
-template <int S, int BLOCK>
+// WT > 0: built for exactly WT ranks (8 and 16 are), the tiles' rank loop
+// unrolled.
+template <int S, int BLOCK, int WT = 0>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void k_reduce_coop_wide(const RArgs a) {
     small_phase<BLOCK>(a.n_small,
@@ -1120,7 +1135,7 @@ void k_reduce_coop_wide(const RArgs a) {
     if (tk < total) {
         float acc[S][RV];
         tc = load_desc(a.tiles, tk);
-        reduce_tile<S, BLOCK, 1, true>(a, tc, acc);
+        reduce_tile<S, BLOCK, 1, true, WT>(a, tc, acc);
         if (a.r) store_sum<S, BLOCK>(tc, acc, a.r);
         mc = block_max<BLOCK>(acc_absmax<S>(acc), sh);
         if (tc.count > 1 && threadIdx.x < 64)
@@ -1138,7 +1153,7 @@ void k_reduce_coop_wide(const RArgs a) {
         float acc_n[S][RV];
         if (more) {
             tnx = load_desc(a.tiles, tn);
-            reduce_tile<S, BLOCK, 1, true>(a, tnx, acc_n);
+            reduce_tile<S, BLOCK, 1, true, WT>(a, tnx, acc_n);
             if (a.r) store_sum<S, BLOCK>(tnx, acc_n, a.r);
             mn = block_max<BLOCK>(acc_absmax<S>(acc_n), sh);
             if (tnx.count > 1 && threadIdx.x < 64) {
@@ -1500,10 +1515,29 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
                : quantize_typed<__half, false>(a, t, s, cap);
 }
 
-template <int S>
+template <int S, int WT = 0>
 constexpr auto coop_reduce_kernel() {
-    if constexpr (S == R_SLOTS_WIDE) return k_reduce_coop_wide<S, R_BLOCK>;
+    if constexpr (S == R_SLOTS_WIDE) return k_reduce_coop_wide<S, R_BLOCK, WT>;
     else return k_reduce_coop<S, R_BLOCK>;
+}
+
+template <int S, int WT>
+hipError_t reduce_persistent(const RArgs &a, const Table &t, int64_t cap, hipStream_t s,
+                             bool &launched) {
+    constexpr auto coop = coop_reduce_kernel<S, WT>();
+    int64_t resident = resident_groups<coop>(R_BLOCK);
+    if (cap > 0 && cap < resident) resident = cap;
+    launched = false;
+    if (resident < t.big_max_count) return hipSuccess;
+    RArgs c = a;
+    c.small = t.d_small;
+    c.n_small = t.n_small;
+    c.tiles = t.d_big;
+    c.n_tiles = t.n_big;
+    const int64_t small_groups = (t.n_small + R_BLOCK / 64 - 1) / (R_BLOCK / 64);
+    const int64_t groups = t.n_big > small_groups ? t.n_big : small_groups;
+    launched = true;
+    return launch_persistent(coop, groups < resident ? groups : resident, R_BLOCK, c, s);
 }
 
 template <int S>
@@ -1533,18 +1567,13 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
         }
         return hipGetLastError();
     }
-    constexpr auto coop = coop_reduce_kernel<S>();
-    int64_t resident = resident_groups<coop>(R_BLOCK);
-    if (cap > 0 && cap < resident) resident = cap;
-    if (!wait_free && resident >= t.big_max_count) {
-        RArgs c = a;
-        c.small = t.d_small;
-        c.n_small = t.n_small;
-        c.tiles = t.d_big;
-        c.n_tiles = t.n_big;
-        const int64_t small_groups = (t.n_small + R_BLOCK / 64 - 1) / (R_BLOCK / 64);
-        const int64_t groups = t.n_big > small_groups ? t.n_big : small_groups;
-        return launch_persistent(coop, groups < resident ? groups : resident, R_BLOCK, c, s);
+    if (!wait_free) {
+        bool launched = false;
+        hipError_t e;
+        if (S == R_SLOTS_WIDE && a.W == 8) e = reduce_persistent<S, 8>(a, t, cap, s, launched);
+        else if (S == R_SLOTS_WIDE && a.W == 16) e = reduce_persistent<S, 16>(a, t, cap, s, launched);
+        else e = reduce_persistent<S, 0>(a, t, cap, s, launched);
+        if (launched || e != hipSuccess) return e;
     }
     if (t.n_multi > 0) {
         RArgs p = a;
@@ -1577,7 +1606,14 @@ int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t) {
 }
 
 int64_t reduce_resident(const Table &t) {
-    if (t.slots == R_SLOTS_WIDE) return resident_groups<coop_reduce_kernel<R_SLOTS_WIDE>()>(R_BLOCK);
+    if (t.slots == R_SLOTS_WIDE) {
+        int64_t r = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 0>()>(R_BLOCK);
+        const int64_t r8 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 8>()>(R_BLOCK);
+        const int64_t r16 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 16>()>(R_BLOCK);
+        if (r8 < r) r = r8;
+        if (r16 < r) r = r16;
+        return r;
+    }
     return resident_groups<coop_reduce_kernel<R_SLOTS_NARROW>()>(R_BLOCK);
 }
 
