@@ -73,8 +73,7 @@ constexpr int kSlotElems[TAB_COUNT] = {4, 8, 16};  // V of each table
 // waves get empty pieces).  The waves of one unit combine their maxima in
 // LDS.
 constexpr int PIECE_WAVES = 8;
-constexpr int PIECE_LANE_SLOTS = 1;
-constexpr int PIECE_SLOTS = 64 * PIECE_LANE_SLOTS;
+constexpr int PIECE_SLOTS = 64;
 
 // Cross-work-group state of the persistent kernels: one published-max word
 // per tile and rank and one result word per multi-tile unit and rank (high

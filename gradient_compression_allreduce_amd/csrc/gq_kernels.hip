@@ -1286,14 +1286,13 @@ __global__ __launch_bounds__(PIECE_WAVES * 64) void k_reduce_pieces(const RArgs 
     __shared__ uint32_t wmax[PIECE_WAVES];
     const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Tile p = load_desc(a.small, static_cast<int64_t>(blockIdx.x) * PIECE_WAVES + v);
-    constexpr int PS = PIECE_LANE_SLOTS;
-    static_assert(PS == 1, "reduce_piece takes one slot per lane");
-    float acc[PS][RV];
+    static_assert(PIECE_SLOTS == 64, "reduce_piece takes one slot per lane");
+    float acc[1][RV];
     uint32_t m = 0;
     if (p.count > 0) {
         reduce_piece(a, p, acc);
-        if (a.r) store_sum<PS, 64>(p, acc, a.r);
-        m = wave_max(acc_absmax<PS>(acc));
+        if (a.r) store_sum<1, 64>(p, acc, a.r);
+        m = wave_max(acc_absmax<1>(acc));
     }
     if ((threadIdx.x & 63) == 0) wmax[v] = m;
     __syncthreads();
@@ -1302,7 +1301,7 @@ __global__ __launch_bounds__(PIECE_WAVES * 64) void k_reduce_pieces(const RArgs 
     for (int i = 0; i < p.count; ++i) um = umax(um, wmax[p.first + i]);
     const float sc = __fdiv_rn(__uint_as_float(um), 127.0f);
     if (v == p.first && (threadIdx.x & 63) == 0) a.scale_out[p.unit] = sc;
-    requantize_tile<PS, 64>(p, acc, quant_params(sc, true), a.q_out);
+    requantize_tile<1, 64>(p, acc, quant_params(sc, true), a.q_out);
 }
 
 enum RMode { R_SUM = 0, R_PASS1 = 1, R_FUSED = 2 };
