@@ -378,7 +378,11 @@ def main():
             same = bool(torch.equal(p_q_out, q_out)) and bool(
                 torch.equal(p_s_out.view(torch.int32), s_out.view(torch.int32)))
             p_ms = p0.elapsed_time(p1) / args.steps
+            sched = gq.gq_pipe_schedule(pipe, kind, w.in_mul)
             pipeline.append({"mode": name, "buckets": int(bounds.size - 1),
+                             "schedule": {gq.GQ_PIPE_SCHED_ALTERNATE: "alternate",
+                                          gq.GQ_PIPE_SCHED_EVENTS: "events",
+                                          gq.GQ_PIPE_SCHED_SERIAL: "serial"}[sched],
                              "ms_per_step": round(p_ms, 4),
                              "value": round(w.W * w.n * w.elem_bytes / (p_ms * 1e-3) / 1e9, 2),
                              "code_slot_bytes_per_rank": int(2 * se),

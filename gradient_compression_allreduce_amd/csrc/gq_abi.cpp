@@ -807,6 +807,58 @@ gq_status gq_pipe_clear_faults(gq_pipe *p) {
     return ok();
 }
 
+// Overlap schedules of gq_pipe_step.  Kernels of two buckets run side by
+// side, so their forms must not strand each other's work groups:
+//  ALTERNATE  buckets alternate between the two streams, each bucket's
+//             reduce right after its quantize on the same stream (code slot
+//             b % 2 is then always used by one stream, and no event orders
+//             the streams inside the step).  Any kernel of one stream may
+//             run beside any kernel of the other, so every kernel that waits
+//             on its own work groups gets a grid of at most the compute unit
+//             count; this needs each such kernel to fit at least two work
+//             groups per compute unit (one of each of two such kernels then
+//             fits in any compute unit that holds fewer than two, and
+//             together they never exceed what the device holds at once).  A
+//             kernel that never waits always finishes and frees its compute
+//             units.
+//  EVENTS     otherwise: quantize on the caller's stream, reduce on the
+//             second stream after an event, so that only bucket b's reduce
+//             and bucket b+1's quantize meet; per such pair, both run in
+//             their full forms if one of them never waits, and else the
+//             reduce takes its form that never waits.
+static bool pipe_alternates(const gq_pipe *p, gq_dtype dt, bool mul, int64_t cus) {
+    for (size_t b = 0; b < p->tab.size(); ++b) {
+        const gq::Table &q = p->tab[b]->tab[q_table(dt)];
+        const gq::Table &r = p->tab[b]->tab[gq::TAB_R];
+        if (gq::quantize_waits(dt, mul, q, 0) && gq::quantize_resident(dt, mul, q) < 2 * cus)
+            return false;
+        if (gq::reduce_waits(r, 0) && gq::reduce_resident(r) < 2 * cus) return false;
+    }
+    return true;
+}
+
+gq_status gq_pipe_schedule(const gq_pipe *p, gq_dtype dt, float in_mul, int32_t *schedule) {
+    const char *op = "gq_pipe_schedule";
+    if (!p) return fail(GQ_ERR_INVALID, op, "plan is NULL");
+    if (!schedule) return fail(GQ_ERR_INVALID, op, "schedule is NULL");
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    if (!std::isfinite(in_mul) || !(in_mul > 0.0f))
+        return fail(GQ_ERR_INVALID, op, "in_mul = %g must be finite and > 0", (double)in_mul);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GQ_ERR_HIP, op, "hipGetDevice failed");
+    if (dev != p->device)
+        return fail(GQ_ERR_DEVICE, op, "current device %d, plan lives on device %d", dev, p->device);
+    if (p->mode == GQ_PIPE_SERIAL) {
+        *schedule = GQ_PIPE_SCHED_SERIAL;
+        return ok();
+    }
+    const int64_t cus = gq::device_cus();
+    if (cus < 1) return fail(GQ_ERR_HIP, op, "device query failed");
+    *schedule = pipe_alternates(p, dt, in_mul != 1.0f, cus) ? GQ_PIPE_SCHED_ALTERNATE
+                                                            : GQ_PIPE_SCHED_EVENTS;
+    return ok();
+}
+
 gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt, float in_mul,
                        int8_t *const *q_slot, float *const *scale_slot, float *scale_out,
                        int8_t *q_out, gq_stream stream) {
@@ -833,33 +885,9 @@ gq_status gq_pipe_step(gq_pipe *p, const void *const *x, int32_t W, gq_dtype dt,
     auto tr = [&](int64_t b) -> const gq::Table & {
         return p->tab[static_cast<size_t>(b)]->tab[gq::TAB_R];
     };
-    // Overlap schedules.  Kernels of two buckets run side by side, so their
-    // forms must not strand each other's work groups:
-    //  ALTERNATE  buckets alternate between the two streams, each bucket's
-    //             reduce right after its quantize on the same stream (code
-    //             slot b % 2 is then always used by one stream, and no event
-    //             orders the streams inside the step).  Any kernel of one
-    //             stream may run beside any kernel of the other, so every
-    //             kernel that waits on its own work groups gets a grid of at
-    //             most the compute unit count; this needs each such kernel
-    //             to fit at least two work groups per compute unit (one of
-    //             each of two such kernels then fits in any compute unit
-    //             that holds fewer than two, and together they never exceed
-    //             what the device holds at once).  A kernel that never
-    //             waits always finishes and frees its compute units.
-    //  EVENTS     otherwise: quantize on the caller's stream, reduce on the
-    //             second stream after an event, so that only bucket b's
-    //             reduce and bucket b+1's quantize meet; per such pair, both
-    //             run in their full forms if one of them never waits, and
-    //             else the reduce takes its form that never waits.
     const int64_t cus = serial ? 0 : gq::device_cus();
     if (!serial && cus < 1) return fail(GQ_ERR_HIP, op, "device query failed");
-    bool alternate = !serial;
-    for (int64_t b = 0; b < B && alternate; ++b) {
-        if (gq::quantize_waits(dt, mul, tq(b), 0) && gq::quantize_resident(dt, mul, tq(b)) < 2 * cus)
-            alternate = false;
-        if (gq::reduce_waits(tr(b), 0) && gq::reduce_resident(tr(b)) < 2 * cus) alternate = false;
-    }
+    const bool alternate = !serial && pipe_alternates(p, dt, mul, cus);
     hipError_t e = hipSuccess;
     if (alternate) {
         // the second stream starts after the caller's stream's earlier work

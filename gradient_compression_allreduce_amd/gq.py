@@ -22,6 +22,7 @@ GQ_F32, GQ_F16 = 0, 1
 GQ_SCHED_LAYER, GQ_SCHED_CHUNK = 0, 1
 GQ_PIPE_OVERLAP, GQ_PIPE_SERIAL = 0, 1
 GQ_FORM_PERSISTENT, GQ_FORM_TWO_PASS, GQ_FORM_SHORT_UNITS = 0, 1, 2
+GQ_PIPE_SCHED_ALTERNATE, GQ_PIPE_SCHED_EVENTS, GQ_PIPE_SCHED_SERIAL = 0, 1, 2
 GQ_MAX_RANKS = 64
 GQ_MAX_TILES = 1 << 22
 GQ_NOALLOC_MAX_MAXIMA = 1 << 20
@@ -33,7 +34,7 @@ EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
            "gq_absmax", "gq_quantize", "gq_quantize_noalloc",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
            "gq_sum_f32", "gq_error_report", "gq_pipe_create", "gq_pipe_destroy",
-           "gq_pipe_slots", "gq_pipe_faults", "gq_pipe_clear_faults", "gq_pipe_step", "gq_chunker_create",
+           "gq_pipe_slots", "gq_pipe_schedule", "gq_pipe_faults", "gq_pipe_clear_faults", "gq_pipe_step", "gq_chunker_create",
            "gq_chunker_destroy", "gq_chunker_update", "gq_chunker_predict", "gq_chunker_plan")
 GQ_STATS = 10
 STATS = ("max_abs_err", "max_abs_ref", "max_rel_err", "sum_abs_err", "sum_abs_ref",
@@ -98,6 +99,8 @@ def _load():
     L.gq_pipe_destroy.argtypes = [vp]
     L.gq_pipe_slots.restype = st
     L.gq_pipe_slots.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.gq_pipe_schedule.restype = st
+    L.gq_pipe_schedule.argtypes = [vp, i32, ctypes.c_float, ctypes.POINTER(i32)]
     L.gq_pipe_faults.restype = st
     L.gq_pipe_faults.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
     L.gq_pipe_clear_faults.restype = st
@@ -578,6 +581,14 @@ def gq_pipe_slots(pipe):
     e, u = ctypes.c_int64(0), ctypes.c_int64(0)
     _check(lib.gq_pipe_slots(pipe.handle, ctypes.byref(e), ctypes.byref(u)))
     return e.value, u.value
+
+
+def gq_pipe_schedule(pipe, dtype_code=GQ_F32, in_mul=1.0):
+    """The schedule gq_pipe_step runs for this plan on the current device:
+    GQ_PIPE_SCHED_ALTERNATE, GQ_PIPE_SCHED_EVENTS or GQ_PIPE_SCHED_SERIAL."""
+    v = ctypes.c_int32(-1)
+    _check(lib.gq_pipe_schedule(pipe.handle, int(dtype_code), float(in_mul), ctypes.byref(v)))
+    return v.value
 
 
 def gq_pipe_faults(pipe):

@@ -397,6 +397,21 @@ gq_status gq_pipe_destroy(gq_pipe *p);
 gq_status gq_pipe_slots(const gq_pipe *p, int64_t *slot_elems, int64_t *slot_units);
 
 /*
+ * gq_pipe_schedule -- which schedule gq_pipe_step runs for this plan with
+ * gradients of type dt and multiplier in_mul on the current device
+ * (informational; see the pipeline comment above): GQ_PIPE_SCHED_ALTERNATE
+ * (buckets alternate between the two streams, waiting kernels' grids
+ * capped at the compute unit count), GQ_PIPE_SCHED_EVENTS (quantizes on the
+ * caller's stream, reduces on the second stream after events) or
+ * GQ_PIPE_SCHED_SERIAL (a GQ_PIPE_SERIAL plan).  Errors: GQ_ERR_INVALID,
+ * GQ_ERR_DEVICE, GQ_ERR_HIP.
+ */
+#define GQ_PIPE_SCHED_ALTERNATE 0
+#define GQ_PIPE_SCHED_EVENTS 1
+#define GQ_PIPE_SCHED_SERIAL 2
+gq_status gq_pipe_schedule(const gq_pipe *p, gq_dtype dt, float in_mul, int32_t *schedule);
+
+/*
  * gq_pipe_faults -- bounded waits that gave up in the plan's persistent
  * launches (see gq_units_faults; the plan's tables keep their counts until
  * gq_pipe_clear_faults).  Synchronizes the device.

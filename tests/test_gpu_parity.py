@@ -511,7 +511,7 @@ def test_random_tables_sweep(gq, oracle):
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
-@pytest.mark.parametrize("W,wide", [(3, False), (16, False), (5, True)])
+@pytest.mark.parametrize("W,wide", [(1, False), (3, False), (16, False), (64, False), (5, True)])
 def test_short_unit_tables(gq, oracle, kind, W, wide):
     """Tables of many short tensors (every unit fits one tile, units of one
     wave's share hold most elements) take the wait-free short-unit form in

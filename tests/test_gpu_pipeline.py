@@ -61,16 +61,25 @@ def run_pipe(gq, pipe, xs, W, in_mul, n, U, reps=1, fresh=None):
             [t.cpu().numpy() for t in s_slots])
 
 
-def check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh=None, mode=None):
+def check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh=None, mode=None,
+               schedule=None):
+    """Both modes (or `mode`) against the oracle; `schedule`, if given, is the
+    schedule the overlap mode must take."""
     if mode is None:
         for m in (gq.GQ_PIPE_OVERLAP, gq.GQ_PIPE_SERIAL):
-            check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh, m)
+            check_pipe(gq, oracle, xs, kind, off, bounds, in_mul, label, fresh, m, schedule)
         return
     label = "%s/mode%d" % (label, mode)
     W = len(xs)
     n = int(off[-1])
     U = off.size - 1
     pipe = gq.gq_pipe_create(off, bounds, mode)
+    sched = gq.gq_pipe_schedule(pipe, kind, in_mul)
+    if mode == gq.GQ_PIPE_SERIAL:
+        assert sched == gq.GQ_PIPE_SCHED_SERIAL, (label, sched)
+    elif schedule is not None:
+        assert sched == schedule, (label, sched)
+    label = "%s/sched%d" % (label, sched)
     final = fresh if fresh is not None else xs
     want = oracle.allreduce_step(final, kind, off, in_mul)
     say("pipeline", label, "W", W, "n", n, "units", U, "buckets", bounds.size - 1)
@@ -201,7 +210,25 @@ def test_pipeline_resnet152_buckets(gq, oracle):
     off = w.toff.copy()
     bounds = np.array([a for a, _ in w.buckets] + [len(w.sizes)], dtype=np.int64)
     xs = [w.fill(r) for r in range(w.W)]
-    check_pipe(gq, oracle, xs, F32, off, bounds, w.in_mul, w.name)
+    check_pipe(gq, oracle, xs, F32, off, bounds, w.in_mul, w.name,
+               schedule=gq.GQ_PIPE_SCHED_ALTERNATE)
+
+
+def test_pipeline_event_schedule(gq, oracle):
+    """A plan whose buckets take the chunk quantize (one work group per
+    compute unit) with a unit of several chunk tiles, so that quantize waits
+    on its own work groups: the overlap mode then keeps the quantizes on the
+    caller's stream and the reduces on the second stream after events, the
+    reduce that meets a waiting quantize in its form that never waits."""
+    rng = np.random.default_rng(450)
+    sizes = [30_000] * 5 + [100_000] + [30_001] * 5 + [100_003] + [29_999] * 5
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    bounds = np.array([0, 6, 12, 17], dtype=np.int64)
+    units = gq.gq_units_create(off[:7])
+    assert gq.gq_units_schedule(units, gq.GQ_F32) == gq.GQ_SCHED_CHUNK
+    xs = [_grad(rng, int(off[-1]), F32) for _ in range(3)]
+    check_pipe(gq, oracle, xs, F32, off, bounds, 1.0, "event_schedule",
+               schedule=gq.GQ_PIPE_SCHED_EVENTS)
 
 
 def test_pipeline_tiny_and_odd_buckets(gq, oracle):
