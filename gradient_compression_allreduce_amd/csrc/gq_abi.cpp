@@ -72,50 +72,86 @@ void build_tiles(const std::vector<int64_t> &off, int V, int64_t cap_slots,
     unit_first[U] = static_cast<int32_t>(tiles.size());
 }
 
-// The per-wave work of a short reduce table (see gq::Table::d_short): each
-// unit of at most PIECE_WAVES * PIECE_SLOTS slots cut into pieces of
-// PIECE_SLOTS slots from its first slot, and the units packed whole into
-// work groups of PIECE_WAVES pieces, best fit in decreasing order of piece
-// count (units are independent, so their order is free, and a work group
-// with idle waves would hold resident slots for nothing); the other units
-// keep their one tile each (a short table has no multi-tile unit).
+// Lanes per unit of a pack for a unit spanning `slots` slots: the smallest
+// power of two from PACK_MIN_LANES up that holds them, or 64 above 32.
+int pack_lanes(int64_t slots) {
+    int g = gq::PACK_MIN_LANES;
+    while (g < 64 && g < slots) g *= 2;
+    return g;
+}
+
+// Packs of the units `us` (all of `lanes` lanes each, in the given order),
+// 64 / lanes units to a pack, appended to packs and their unit tiles to
+// units (first: the unit's index in that list).
+void add_packs(const std::vector<int64_t> &off, const std::vector<int64_t> &us, int lanes,
+               std::vector<gq::Pack> &packs, std::vector<gq::Tile> &units) {
+    const size_t per = static_cast<size_t>(64 / lanes);
+    for (size_t i = 0; i < us.size(); i += per) {
+        const size_t cnt = std::min(per, us.size() - i);
+        packs.push_back({static_cast<int32_t>(units.size()), static_cast<int32_t>(cnt), lanes, 0});
+        for (size_t k = 0; k < cnt; ++k) {
+            const int64_t u = us[i + k];
+            units.push_back({off[u], off[u + 1], static_cast<int32_t>(u),
+                             static_cast<int32_t>(units.size()), 1, -1});
+        }
+    }
+}
+
+// The per-wave work of a short reduce table (see gq::Table::d_short).  A unit
+// of at most 32 slots goes into a pack (several to a wave).  A unit of more
+// than 32 and at most PIECE_WAVES * PIECE_SLOTS slots is cut into pieces of
+// PIECE_SLOTS slots from its first slot.  Pieces and packs' waves are
+// packed, each unit's pieces whole, into work groups of PIECE_WAVES waves,
+// best fit in decreasing order of piece count (units are independent, so
+// their order is free, and a work group with idle waves would hold
+// resident slots for nothing).  The other units keep their one tile each (a
+// short table has no multi-tile unit).
 void build_pieces(const std::vector<int64_t> &off, int V, const std::vector<gq::Tile> &tiles,
                   const std::vector<int32_t> &unit_first, std::vector<gq::Tile> &pieces,
+                  std::vector<gq::Pack> &packs, std::vector<gq::Tile> &pack_units,
                   std::vector<gq::Tile> &rest) {
     constexpr int PW = gq::PIECE_WAVES;
     constexpr int64_t PS = gq::PIECE_SLOTS;
     const int64_t U = static_cast<int64_t>(off.size()) - 1;
-    auto count = [&](int64_t u) {
-        return (((off[u + 1] + V - 1) / V - off[u] / V) + PS - 1) / PS;
-    };
-    // units by piece count, most first (counting sort, unit order within)
+    auto span = [&](int64_t u) { return (off[u + 1] + V - 1) / V - off[u] / V; };
+    // units by piece count, most first (counting sort, unit order within);
+    // packs of the smallest units, one wave each
     std::vector<std::vector<int64_t>> by_k(PW + 1);
+    std::vector<std::vector<int64_t>> by_lanes(7);  // index log2(lanes)
     for (int64_t u = 0; u < U; ++u) {
-        const int64_t k = count(u);
+        const int64_t sl = span(u);
+        const int64_t k = (sl + PS - 1) / PS;
         if (k > PW) {
             gq::Tile tl = tiles[unit_first[u]];
             tl.first = static_cast<int32_t>(rest.size());
             rest.push_back(tl);
+        } else if (sl <= 32) {
+            by_lanes[__builtin_ctz(static_cast<unsigned>(pack_lanes(sl)))].push_back(u);
         } else {
             by_k[k].push_back(u);
         }
     }
+    for (int lg = 5; lg >= 2; --lg) add_packs(off, by_lanes[lg], 1 << lg, packs, pack_units);
     std::vector<std::vector<gq::Tile>> groups;
     std::vector<std::vector<int64_t>> with_free(PW);  // groups by free waves (1 .. PW-1)
+    auto place = [&](int k) -> std::vector<gq::Tile> & {
+        int c = k;
+        while (c < PW && with_free[c].empty()) ++c;
+        int64_t g;
+        if (c < PW) {
+            g = with_free[c].back();
+            with_free[c].pop_back();
+        } else {
+            g = static_cast<int64_t>(groups.size());
+            groups.emplace_back();
+            c = PW;
+        }
+        if (c - k > 0) with_free[c - k].push_back(g);
+        return groups[g];
+    };
     for (int k = PW; k >= 1; --k) {
         for (const int64_t u : by_k[k]) {
-            int c = k;
-            while (c < PW && with_free[c].empty()) ++c;
-            int64_t g;
-            if (c < PW) {
-                g = with_free[c].back();
-                with_free[c].pop_back();
-            } else {
-                g = static_cast<int64_t>(groups.size());
-                groups.emplace_back();
-                c = PW;
-            }
-            std::vector<gq::Tile> &grp = groups[g];
+            std::vector<gq::Tile> &grp = place(k);
             const int32_t first = static_cast<int32_t>(grp.size());
             const int64_t a = off[u], b = off[u + 1], j0 = a / V;
             for (int i = 0; i < k; ++i) {
@@ -123,7 +159,10 @@ void build_pieces(const std::vector<int64_t> &off, int V, const std::vector<gq::
                 grp.push_back({pb > a ? pb : a, pe < b ? pe : b, static_cast<int32_t>(u), first, k,
                                -1});
             }
-            if (c - k > 0) with_free[c - k].push_back(g);
+        }
+        if (k == 1) {
+            for (size_t i = 0; i < packs.size(); ++i)
+                place(1).push_back({0, 0, -1, static_cast<int32_t>(i), 1, gq::PACK_WAVE});
         }
     }
     const gq::Tile empty = {0, 0, -1, 0, 0, -1};
@@ -134,23 +173,27 @@ void build_pieces(const std::vector<int64_t> &off, int V, const std::vector<gq::
     }
 }
 
-// The per-wave work of a short quantize table: the units of at most
-// cap_slots slots, one entry each (first: its index in the list); the other
-// units keep their one tile each.
+// The per-wave work of a short quantize table: packs of the units of at
+// most cap_slots slots (a unit of more than 32 slots alone in a pack of 64
+// lanes; those first, the larger ones taking longer), their units in pack
+// order; the other units keep their one tile each.
 void build_short_units(const std::vector<int64_t> &off, int V, int64_t cap_slots,
                        const std::vector<gq::Tile> &tiles, const std::vector<int32_t> &unit_first,
-                       std::vector<gq::Tile> &work, std::vector<gq::Tile> &rest) {
+                       std::vector<gq::Pack> &packs, std::vector<gq::Tile> &units,
+                       std::vector<gq::Tile> &rest) {
     const int64_t U = static_cast<int64_t>(off.size()) - 1;
+    std::vector<std::vector<int64_t>> by_lanes(7);  // index log2(lanes)
     for (int64_t u = 0; u < U; ++u) {
-        const int64_t a = off[u], b = off[u + 1];
-        if ((b + V - 1) / V - a / V <= cap_slots) {
-            work.push_back({a, b, static_cast<int32_t>(u), static_cast<int32_t>(work.size()), 1, -1});
+        const int64_t sl = (off[u + 1] + V - 1) / V - off[u] / V;
+        if (sl <= cap_slots) {
+            by_lanes[__builtin_ctz(static_cast<unsigned>(pack_lanes(sl)))].push_back(u);
         } else {
             gq::Tile tl = tiles[unit_first[u]];
             tl.first = static_cast<int32_t>(rest.size());
             rest.push_back(tl);
         }
     }
+    for (int lg = 6; lg >= 2; --lg) add_packs(off, by_lanes[lg], 1 << lg, packs, units);
 }
 
 template <typename T>
@@ -174,6 +217,8 @@ void free_table(gq::Table &t) {
     if (t.d_res) (void)hipFree(t.d_res);
     if (t.d_cnt) (void)hipFree(t.d_cnt);
     if (t.d_short) (void)hipFree(t.d_short);
+    if (t.d_packs) (void)hipFree(t.d_packs);
+    if (t.d_pack_units) (void)hipFree(t.d_pack_units);
     if (t.d_rest) (void)hipFree(t.d_rest);
     t = gq::Table{};
 }
@@ -399,12 +444,20 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             t.small_dominant = 2 * in_small > off[n_units] - off[0];
         }
         if (gq::short_table(t)) {
-            std::vector<gq::Tile> work, rest;
-            if (ti == gq::TAB_R) build_pieces(off, V, tiles, unit_first, work, rest);
-            else build_short_units(off, V, 64 * gq::SHORT_SLOTS_Q, tiles, unit_first, work, rest);
+            std::vector<gq::Tile> work, pack_units, rest;
+            std::vector<gq::Pack> packs;
+            if (ti == gq::TAB_R)
+                build_pieces(off, V, tiles, unit_first, work, packs, pack_units, rest);
+            else
+                build_short_units(off, V, 64 * gq::SHORT_SLOTS_Q, tiles, unit_first, packs, work,
+                                  rest);
             t.n_short = static_cast<int64_t>(work.size());
+            t.n_packs = static_cast<int64_t>(packs.size());
+            t.n_pack_units = static_cast<int64_t>(pack_units.size());
             t.n_rest = static_cast<int64_t>(rest.size());
             e = upload(&t.d_short, work);
+            if (e == hipSuccess) e = upload(&t.d_packs, packs);
+            if (e == hipSuccess) e = upload(&t.d_pack_units, pack_units);
             if (e == hipSuccess) e = upload(&t.d_rest, rest);
         }
         if (e == hipSuccess) e = upload(&t.d_tiles, tiles);

@@ -75,6 +75,25 @@ constexpr int kSlotElems[TAB_COUNT] = {4, 8, 16};  // V of each table
 constexpr int PIECE_WAVES = 8;
 constexpr int PIECE_SLOTS = 64;
 
+// Short tables pack units of at most 32 slots several to a wave: a pack
+// holds up to 64 / lanes units of at most `lanes` slots (lanes = 4, 8, 16 or
+// 32), each taken by its own group of `lanes` lanes, one slot per lane,
+// which combine their maxima by shuffles within the group.  (One unit per
+// wave would leave most of its lanes idle and pay a wave's whole chain of
+// memory round trips for a few elements.)  In a quantize table, a pack
+// with lanes = 64 holds one larger unit, taken by the whole wave.
+struct Pack {
+    int32_t first;   // index of the pack's first unit in the table's pack unit list
+    int32_t count;   // units in the pack
+    int32_t lanes;   // lanes per unit (a power of two, 4 .. 64)
+    int32_t pad;
+};
+static_assert(sizeof(Pack) == 16, "Pack layout");
+constexpr int PACK_MIN_LANES = 4;
+// A wave of a short reduce table's piece list that takes a pack: its
+// entry's slot field holds PACK_WAVE and its first field the pack's index.
+constexpr int32_t PACK_WAVE = -2;
+
 // Cross-work-group state of the persistent kernels: one published-max word
 // per tile and rank and one result word per multi-tile unit and rank (high
 // half: the launch's tag, low half: a max), one arrival counter per
@@ -97,16 +116,22 @@ struct Table {
     Tile *d_big = nullptr;          // [n_big], unit order (first: index into d_big)
     int32_t big_max_count = 1;      // largest tile count of a unit in d_big
     bool small_dominant = false;    // small units hold most elements
-    // short tables only: the per-wave work list and the tiles of the units
-    // it leaves out (first: index into d_rest).  Quantize tables: the units
-    // of at most 64 * SHORT_SLOTS_Q slots, one entry each.  Reduce
-    // table: the pieces of the units of at most PIECE_WAVES * PIECE_SLOTS
-    // slots, PIECE_WAVES per work group (a piece: the unit's elements in its
-    // slot range; first = the wave of the group that holds the unit's first
-    // piece, count = the unit's pieces; an unused wave's piece has count 0;
-    // n_short is a multiple of PIECE_WAVES).
+    // short tables only: the per-wave work and the tiles of the units it
+    // leaves out (first: index into d_rest).  Quantize tables: packs (one
+    // item per rank and pack) of the units of at most 64 * SHORT_SLOTS_Q
+    // slots.  Reduce table: the pieces of the units of more than 32 and at
+    // most PIECE_WAVES * PIECE_SLOTS slots, and the packs of the smaller
+    // units, PIECE_WAVES waves per work group (a piece: the unit's elements
+    // in its slot range; first = the wave of the group that holds the
+    // unit's first piece, count = the unit's pieces; a pack's wave: slot =
+    // PACK_WAVE, first = the pack's index; an unused wave's entry has count
+    // 0 and slot -1; n_short is a multiple of PIECE_WAVES).
     int64_t n_short = 0;
-    Tile *d_short = nullptr;
+    Tile *d_short = nullptr;        // quantize: the packs' units; reduce: the waves
+    int64_t n_packs = 0;
+    Pack *d_packs = nullptr;
+    int64_t n_pack_units = 0;       // reduce: the packs' units
+    Tile *d_pack_units = nullptr;
     int64_t n_rest = 0;
     Tile *d_rest = nullptr;
     int32_t *d_multi = nullptr;     // [n_multi] indices of multi tiles
@@ -133,7 +158,8 @@ inline bool table_ready(const Table &t, int64_t n_units) {
         return false;
     if (t.n_multi_units > 0 && (!t.d_pub || !t.d_res || !t.d_cnt)) return false;
     if (short_table(t) && (t.n_short + t.n_rest < 1 || (t.n_short > 0 && !t.d_short) ||
-                           (t.n_rest > 0 && !t.d_rest)))
+                           (t.n_rest > 0 && !t.d_rest) || (t.n_packs > 0 && !t.d_packs) ||
+                           (t.n_pack_units > 0 && !t.d_pack_units)))
         return false;
     return t.block > 0 && t.slots > 0;
 }
@@ -157,8 +183,10 @@ struct QArgs {
     int8_t *q[GQ_MAX_RANKS];
     const Tile *tiles;
     const int32_t *list;        // NULL: blockIdx.x is the tile index
-    const Tile *small;          // small units (one wave each)
+    const Tile *small;          // small units (one wave each); short tables: the packs' units
     int64_t n_small;
+    const Pack *packs;          // short tables
+    int64_t n_packs;
     uint32_t *partial;          // [W][n_tiles]
     const uint32_t *amax;       // [W][n_units] or NULL
     const int32_t *unit_first;  // for the finalize step
@@ -181,8 +209,10 @@ struct RArgs {
     const float *scale[GQ_MAX_RANKS];
     const Tile *tiles;
     const int32_t *list;
-    const Tile *small;          // small units (one wave each)
+    const Tile *small;          // small units (one wave each); short tables: the waves
     int64_t n_small;
+    const Pack *packs;          // short tables
+    const Tile *pack_units;     // short tables: the packs' units
     uint32_t *partial;          // [n_tiles]
     float *r;                   // NULL or [n]
     float *scale_out;           // [n_units]

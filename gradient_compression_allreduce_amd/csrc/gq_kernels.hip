@@ -337,6 +337,18 @@ __device__ __forceinline__ uint32_t unit_max(uint64_t *pub, uint64_t *res, int32
     return mx;
 }
 
+// Pack descriptors, likewise (the same for the whole wave).
+__device__ __forceinline__ Pack load_pack(const Pack *packs, int64_t i) {
+    using ConstPack = __attribute__((address_space(4))) const Pack;
+    const ConstPack *p = (const ConstPack *)(packs + i);
+    Pack k;
+    k.first = p->first;
+    k.count = p->count;
+    k.lanes = p->lanes;
+    k.pad = 0;
+    return k;
+}
+
 // Tile descriptors are read-only: load them through the scalar cache.
 __device__ __forceinline__ Tile load_desc(const Tile *tiles, int64_t i) {
     using ConstTile = __attribute__((address_space(4))) const Tile;
@@ -354,17 +366,72 @@ __device__ __forceinline__ Tile load_desc(const Tile *tiles, int64_t i) {
 // ---- quantize kernels -------------------------------------------------------------
 
 // Small units: one wave per (rank, unit), no tile exchange and no ticket.
-// `item` runs over ranks, then small units.
 template <typename TIn, int SS, bool MUL>
-__device__ __forceinline__ void quantize_small_unit(const QArgs &a, int64_t item) {
+__device__ __forceinline__ void quantize_wave_unit(const QArgs &a, int w, const Tile &t) {
     using Raw = typename In<TIn>::Raw;
-    const int w = static_cast<int>(item / a.n_small);
-    const Tile t = load_desc(a.small, item - static_cast<int64_t>(w) * a.n_small);
     Raw raw[SS];
     const uint32_t m = wave_max(load_tile<TIn, SS, 64, true>(a.x[w], t, a.n, raw));
     const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
     if ((threadIdx.x & 63) == 0) a.scale[w][t.unit] = sc;
     quantize_tile<TIn, SS, 64, MUL>(raw, t, a.in_mul, quant_params(sc, true), a.q[w]);
+}
+
+// `item` runs over ranks, then small units.
+template <typename TIn, int SS, bool MUL>
+__device__ __forceinline__ void quantize_small_unit(const QArgs &a, int64_t item) {
+    const int w = static_cast<int>(item / a.n_small);
+    quantize_wave_unit<TIn, SS, MUL>(a, w, load_desc(a.small, item - static_cast<int64_t>(w) * a.n_small));
+}
+
+// The lane's group of a pack of lanes < 64 (group g = lane / lanes takes
+// the pack's unit g, if there is one): its unit's tile (a vector load, the
+// units differing across the wave), its lane within the group, and whether
+// it has a unit.
+struct PackLane {
+    Tile t;
+    int li;
+    bool live;
+};
+__device__ __forceinline__ PackLane pack_lane(const Tile *units, const Pack &pk) {
+    PackLane pl;
+    const int lane = threadIdx.x & 63;
+    const int lg = __builtin_ctz(static_cast<unsigned>(pk.lanes));
+    const int g = lane >> lg;
+    pl.li = lane & (pk.lanes - 1);
+    pl.live = g < pk.count;
+    pl.t = Tile{0, 0, 0, 0, 0, -1};
+    if (pl.live) pl.t = units[pk.first + g];
+    return pl;
+}
+
+// Max over each group of `lanes` lanes (a power of two): the xor partners
+// of offsets below `lanes` stay within the group.
+__device__ __forceinline__ uint32_t group_max(uint32_t v, int lanes) {
+    for (int o = lanes >> 1; o > 0; o >>= 1)
+        v = umax(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64)));
+    return v;
+}
+
+// A pack of lanes < 64 of a short quantize table: each group of lanes
+// quantizes its unit, one slot per lane.
+template <typename TIn, bool MUL>
+__device__ __forceinline__ void quantize_pack(const QArgs &a, int w, const Pack &pk) {
+    constexpr int V = In<TIn>::V;
+    const PackLane pl = pack_lane(a.small, pk);
+    const Tile &t = pl.t;
+    const int64_t j = t.begin / V + pl.li, j1 = (t.end + V - 1) / V;
+    const bool in = pl.live && j < j1;
+    typename In<TIn>::Raw raw{};
+    if (in) raw = In<TIn>::load(a.x[w], j, t.begin, t.end, a.n);
+    const uint32_t m = group_max(In<TIn>::absmax(raw, 0u), pk.lanes);
+    const float sc = __fdiv_rn(In<TIn>::max_value(m, a.in_mul, MUL), 127.0f);
+    if (pl.live && pl.li == 0) a.scale[w][t.unit] = sc;
+    if (in) {
+        const QuantParams qp = quant_params(sc, true);
+        if (qp.mode == CM_FAST) quantize_slot<TIn, MUL, CM_FAST>(raw, j, t, a.in_mul, qp, a.q[w]);
+        else if (qp.mode == CM_EXACT) quantize_slot<TIn, MUL, CM_EXACT>(raw, j, t, a.in_mul, qp, a.q[w]);
+        else quantize_slot<TIn, MUL, CM_ZERO>(raw, j, t, a.in_mul, qp, a.q[w]);
+    }
 }
 
 // The small units' phase of the persistent kernels: wave v of work group g
@@ -870,6 +937,24 @@ __device__ __forceinline__ uint32_t acc_absmax(const float (&acc)[S][RV]) {
     return m;
 }
 
+// The 16 sums of slot j of tile t (acc, one slot's sums), stored where they
+// fall inside the tile.
+__device__ __forceinline__ void store_sum_slot(int64_t j, const Tile &t, const float *acc,
+                                               float *r) {
+    const int64_t i0 = j * RV;
+    float4 f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        f[k] = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
+    if (i0 >= t.begin && i0 + RV <= t.end) {
+        float4 *rp = reinterpret_cast<float4 *>(r + i0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rp[k] = f[k];
+    } else {
+        store_sum_part(r, i0, t.begin, t.end, f[0], f[1], f[2], f[3]);
+    }
+}
+
 template <int S, int BLOCK>
 __device__ __forceinline__ void store_sum(const Tile &t, const float (&acc)[S][RV], float *r) {
     const int64_t tid = opaque_tid<BLOCK>();
@@ -878,19 +963,30 @@ __device__ __forceinline__ void store_sum(const Tile &t, const float (&acc)[S][R
     for (int s = 0; s < S; ++s) {
         const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
         if (j >= j1) continue;
-        const int64_t i0 = j * RV;
-        float4 f[4];
+        store_sum_slot(j, t, acc[s], r);
+    }
+}
+
+// Codes of the 16 sums of slot j of tile t (acc, one slot's sums), stored
+// where they fall inside the tile.
+template <int MODE>
+__device__ __forceinline__ void requantize_slot(int64_t j, const Tile &t, const float *acc,
+                                                const QuantParams &p, int8_t *q) {
+    uint32_t w4[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            f[k] = make_float4(acc[s][4 * k], acc[s][4 * k + 1], acc[s][4 * k + 2], acc[s][4 * k + 3]);
-        if (i0 >= t.begin && i0 + RV <= t.end) {
-            float4 *rp = reinterpret_cast<float4 *>(r + i0);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) rp[k] = f[k];
+    for (int k = 0; k < 4; ++k) {
+        const float *g = acc + 4 * k;
+        if constexpr (MODE == CM_FAST) {
+            w4[k] = codes4_fast(g[0], g[1], g[2], g[3], p.s, p.r);
         } else {
-            store_sum_part(r, i0, t.begin, t.end, f[0], f[1], f[2], f[3]);
+            w4[k] = pack4(code_of<MODE>(g[0], p), code_of<MODE>(g[1], p),
+                          code_of<MODE>(g[2], p), code_of<MODE>(g[3], p));
         }
     }
+    const int64_t i0 = j * RV;
+    const uint4 pk = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    if (i0 >= t.begin && i0 + RV <= t.end) store_stream(q + i0, pk);
+    else store_codes_part(q, i0, RV, t.begin, t.end, pk);
 }
 
 template <int S, int BLOCK, int MODE>
@@ -902,21 +998,7 @@ __device__ __forceinline__ void requantize_tile_mode(const Tile &t, const float 
     for (int s = 0; s < S; ++s) {
         const int64_t j = j0 + static_cast<int64_t>(s) * BLOCK + tid;
         if (j >= j1) continue;
-        uint32_t w4[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float *g = &acc[s][4 * k];
-            if constexpr (MODE == CM_FAST) {
-                w4[k] = codes4_fast(g[0], g[1], g[2], g[3], p.s, p.r);
-            } else {
-                w4[k] = pack4(code_of<MODE>(g[0], p), code_of<MODE>(g[1], p),
-                              code_of<MODE>(g[2], p), code_of<MODE>(g[3], p));
-            }
-        }
-        const int64_t i0 = j * RV;
-        const uint4 pk = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-        if (i0 >= t.begin && i0 + RV <= t.end) store_stream(q + i0, pk);
-        else store_codes_part(q, i0, RV, t.begin, t.end, pk);
+        requantize_slot<MODE>(j, t, acc[s], p, q);
     }
 }
 
@@ -1210,8 +1292,11 @@ template <typename TIn, bool MUL>
 __global__ __launch_bounds__(SMALL_BLOCK) void k_quantize_small(const QArgs a) {
     const int64_t item = static_cast<int64_t>(blockIdx.x) * (SMALL_BLOCK / 64) +
                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= static_cast<int64_t>(a.W) * a.n_small) return;
-    quantize_small_unit<TIn, SHORT_SLOTS_Q, MUL>(a, item);
+    if (item >= static_cast<int64_t>(a.W) * a.n_packs) return;
+    const int w = static_cast<int>(item / a.n_packs);
+    const Pack pk = load_pack(a.packs, item - static_cast<int64_t>(w) * a.n_packs);
+    if (pk.lanes == 64) quantize_wave_unit<TIn, SHORT_SLOTS_Q, MUL>(a, w, load_desc(a.small, pk.first));
+    else quantize_pack<TIn, MUL>(a, w, pk);
 }
 
 // Rank-order dequant-accumulate of one wave's piece (at most 64 slots, one
@@ -1275,6 +1360,75 @@ __device__ __forceinline__ void reduce_piece(const RArgs &a, const Tile &t, floa
     }
 }
 
+// A pack's wave of a short reduce table: each group of lanes sums and
+// requantizes its unit, one slot per lane, four ranks at a time (fewer
+// registers than the pieces' eight, which would cost the kernel
+// occupancy).  The ranks' scales differ across the wave (one unit per
+// group), so they are vector loads, issued before the ranks' code loads
+// (the in-order load count then lets each rank wait for its own loads
+// only).  Lanes without a slot load rank 0's first slot (in every buffer,
+// never used).
+__device__ __forceinline__ void reduce_pack(const RArgs &a, const Pack &pk) {
+    const PackLane pl = pack_lane(a.pack_units, pk);
+    const Tile &t = pl.t;
+    const int64_t j = t.begin / RV + pl.li, j1 = (t.end + RV - 1) / RV;
+    const bool in = pl.live && j < j1;
+    const int64_t nfull = a.n / RV;
+    const int64_t js = (in && j < nfull) ? j : 0;
+    const int32_t u = pl.live ? t.unit : 0;
+    float sums[1][RV];
+    float *acc = sums[0];
+#pragma unroll
+    for (int k = 0; k < RV; ++k) acc[k] = 0.0f;
+    constexpr int PR = 4;
+    for (int w0 = 0; w0 < a.W; w0 += PR) {
+        const int nr = a.W - w0 < PR ? a.W - w0 : PR;
+        float sw[PR];
+#pragma unroll
+        for (int r = 0; r < PR; ++r) sw[r] = a.scale[r < nr ? w0 + r : w0][u];
+        uint4 v[PR];
+        if (nfull > 0) {
+#pragma unroll
+            for (int r = 0; r < PR; ++r)
+                v[r] = load_stream(reinterpret_cast<const uint4 *>(a.q[r < nr ? w0 + r : w0]) + js);
+        }
+#pragma unroll
+        for (int r = 0; r < PR; ++r) {
+            if (r >= nr) break;
+            const uint4 c[1] = {v[r]};
+            accumulate<1>(c, sw[r], sums);
+        }
+    }
+    if (in && j >= nfull) {
+        // the buffer's short last slot, from its bytes, in rank order
+#pragma unroll
+        for (int k = 0; k < RV; ++k) acc[k] = 0.0f;
+        for (int w = 0; w < a.W; ++w) {
+            const uint4 c[1] = {load_tail16(a.q[w], j * RV, a.n)};
+            accumulate<1>(c, a.scale[w][u], sums);
+        }
+    }
+    // elements outside the unit never reach a max or a store
+#pragma unroll
+    for (int k = 0; k < RV; ++k) {
+        const int64_t i = j * RV + k;
+        if (!(in && i >= t.begin && i < t.end)) acc[k] = 0.0f;
+    }
+    if (in && a.r) store_sum_slot(j, t, acc, a.r);
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < RV; ++k) m = umax(m, __float_as_uint(acc[k]) & kAbsMask);
+    m = group_max(m, pk.lanes);
+    const float sc = __fdiv_rn(__uint_as_float(m), 127.0f);
+    if (pl.live && pl.li == 0) a.scale_out[t.unit] = sc;
+    if (in) {
+        const QuantParams qp = quant_params(sc, true);
+        if (qp.mode == CM_FAST) requantize_slot<CM_FAST>(j, t, acc, qp, a.q_out);
+        else if (qp.mode == CM_EXACT) requantize_slot<CM_EXACT>(j, t, acc, qp, a.q_out);
+        else requantize_slot<CM_ZERO>(j, t, acc, qp, a.q_out);
+    }
+}
+
 // Short reduce tables: one wave per piece of PIECE_SLOTS slots (eight
 // ranks' loads in flight, reduce_piece), the waves of a unit in one work
 // group.  Each wave's max goes through LDS to the unit's other waves, and
@@ -1287,6 +1441,11 @@ __global__ __launch_bounds__(PIECE_WAVES * 64) void k_reduce_pieces(const RArgs 
     const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Tile p = load_desc(a.small, static_cast<int64_t>(blockIdx.x) * PIECE_WAVES + v);
     static_assert(PIECE_SLOTS == 64, "reduce_piece takes one slot per lane");
+    if (p.slot == PACK_WAVE) {  // a pack: no unit shared with another wave
+        reduce_pack(a, load_pack(a.packs, p.first));
+        __syncthreads();  // the group's one barrier, as the piece waves'
+        return;
+    }
     float acc[1][RV];
     uint32_t m = 0;
     if (p.count > 0) {
@@ -1412,11 +1571,13 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s, int64_t 
     }
     if (short_table(t)) {
         // many short tensors: no exchange needed (see k_quantize_small)
-        if (t.n_short > 0) {
+        if (t.n_packs > 0) {
             QArgs c = a;
             c.small = t.d_short;
             c.n_small = t.n_short;
-            const int64_t items = static_cast<int64_t>(a.W) * t.n_short;
+            c.packs = t.d_packs;
+            c.n_packs = t.n_packs;
+            const int64_t items = static_cast<int64_t>(a.W) * t.n_packs;
             hipLaunchKernelGGL((k_quantize_small<TIn, MUL>),
                                dim3(static_cast<unsigned>((items + SMALL_BLOCK / 64 - 1) / (SMALL_BLOCK / 64))),
                                dim3(SMALL_BLOCK), 0, s, c);
@@ -1555,6 +1716,8 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
             RArgs c = a;
             c.small = t.d_short;
             c.n_small = t.n_short;
+            c.packs = t.d_packs;
+            c.pack_units = t.d_pack_units;
             hipLaunchKernelGGL(k_reduce_pieces, dim3(static_cast<unsigned>(t.n_short / PIECE_WAVES)),
                                dim3(PIECE_WAVES * 64), 0, s, c);
         }

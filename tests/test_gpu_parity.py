@@ -511,6 +511,33 @@ def test_random_tables_sweep(gq, oracle):
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("W", [3, 8])
+def test_tiny_unit_packs(gq, oracle, kind, W):
+    """Tables of tiny tensors take packs: several units to a wave, each in
+    its own group of 4, 8, 16 or 32 lanes (quantize: units of at most 32
+    slots of 4 or 8 elements; reduce: of at most 32 slots of 16 codes).
+    Sizes around every group boundary at every offset, a pack's last group
+    short of units, all-zero units, and units of more than 32 slots beside
+    them."""
+    rng = np.random.default_rng(700 + W + 10 * kind)
+    lens = list(rng.integers(1, 600, 3000))
+    lens += [1, 2, 3, 4, 5, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+             511, 512, 513, 1024, 2000] * 4
+    rng.shuffle(lens)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(W)]
+    for u in rng.choice(len(lens), 40, replace=False):   # zero units on every rank
+        for x in xs:
+            x[off[u]:off[u + 1]] = 0
+    units = gq.gq_units_create(off)
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    plan = gq.gq_units_launch_plan(units, kind, in_mul)
+    assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_SHORT_UNITS, plan
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "tiny_packs_W%d_k%d" % (W, kind))
+
+
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
 @pytest.mark.parametrize("W,wide", [(1, False), (3, False), (16, False), (64, False), (5, True)])
 def test_short_unit_tables(gq, oracle, kind, W, wide):
     """Tables of many short tensors (every unit fits one tile, units of one
