@@ -127,7 +127,9 @@ def stage_kernels(gq, units, kind, in_mul):
     elif plan["r_form"] == gq.GQ_FORM_TWO_PASS:
         rkernel = "k_reduce"
     else:
-        rkernel = "k_reduce_coop_wide" if gq.gq_units_reduce_tile(units) == 16384 else "k_reduce_coop"
+        # wide (16384-element) and chunk-wide (32768) tiles: one kernel
+        # template on 512 and 1024 threads
+        rkernel = "k_reduce_coop" if gq.gq_units_reduce_tile(units) == 8192 else "k_reduce_coop_wide"
     return qkernel, rkernel
 
 

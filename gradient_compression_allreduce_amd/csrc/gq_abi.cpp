@@ -374,16 +374,20 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
         auto span = [&](int64_t u) { return (off[u + 1] + V - 1) / V - off[u] / V; };
         if (ti == gq::TAB_R) {
             // wide tiles when most elements of the non-small units sit in
-            // units wider than a narrow tile
+            // units wider than a narrow tile; chunk-wide ones when most sit
+            // in units that fill one chunk-wide tile but not one wide tile
             const int64_t narrow = static_cast<int64_t>(gq::R_BLOCK) * gq::R_SLOTS_NARROW;
-            int64_t in_wide = 0, in_big = 0;
+            const int64_t wide = static_cast<int64_t>(gq::R_BLOCK) * gq::R_SLOTS_WIDE;
+            const int64_t chunk = static_cast<int64_t>(gq::R_BLOCK_CHUNK) * gq::R_SLOTS_WIDE;
+            int64_t in_wide = 0, in_chunk = 0, in_big = 0;
             for (int64_t u = 0; u < n_units; ++u) {
                 if (span(u) <= small_cap) continue;
                 in_big += off[u + 1] - off[u];
                 if (span(u) > narrow) in_wide += off[u + 1] - off[u];
+                if (span(u) > wide && span(u) <= chunk) in_chunk += off[u + 1] - off[u];
             }
             t.sched = gq::SCHED_LAYER;
-            t.block = gq::R_BLOCK;
+            t.block = (2 * in_chunk >= in_big && in_big > 0) ? gq::R_BLOCK_CHUNK : gq::R_BLOCK;
             t.slots = (2 * in_wide >= in_big) ? gq::R_SLOTS_WIDE : gq::R_SLOTS_NARROW;
             // the narrow kernel's waves also take units of up to twice their
             // slots, in two halves

@@ -53,6 +53,11 @@ constexpr int R_BLOCK = 512;
 // most of a wide tile's lanes idle.
 constexpr int R_SLOTS_NARROW = 1;
 constexpr int R_SLOTS_WIDE = 2;
+// Chunk-wide reduce tiles: two slots on 1024 threads (32768 elements, one
+// whole 128 KiB fp32 chunk of the chunk plan), for tables whose non-small
+// elements sit mostly in units of that size: each such unit is one tile,
+// summed and requantized with no exchange between work groups.
+constexpr int R_BLOCK_CHUNK = 1024;
 
 // Units whose 16-byte slots span at most 64 * SMALL_SLOTS[table] slots are
 // "small": one wave handles a whole unit, in a phase of its own of the

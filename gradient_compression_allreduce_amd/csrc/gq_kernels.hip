@@ -1174,7 +1174,8 @@ void k_reduce_coop(const RArgs a) {
 // Each lane parks its own sums (as 16-byte words, lane-contiguous, so the
 // stores and loads are free of bank conflicts) and reads back only its own,
 // so parking needs no barrier.  Two tiles of sums would not fit in
-// registers next to a tile's loads; in LDS they take 64 KiB per work group.
+// registers next to a tile's loads; in LDS they take 128 bytes per lane
+// (64 KiB for 512 lanes, 128 KiB for the 1024 lanes of a chunk-wide tile).
 // WT > 0: built for exactly WT ranks (8 and 16 are), the tiles' rank loop
 // unrolled.
 template <int S, int BLOCK, int WT = 0>
@@ -1675,17 +1676,17 @@ hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStrea
                : quantize_typed<__half, false>(a, t, s, cap);
 }
 
-template <int S, int WT = 0>
+template <int S, int BLOCK, int WT = 0>
 constexpr auto coop_reduce_kernel() {
-    if constexpr (S == R_SLOTS_WIDE) return k_reduce_coop_wide<S, R_BLOCK, WT>;
-    else return k_reduce_coop<S, R_BLOCK>;
+    if constexpr (S == R_SLOTS_WIDE) return k_reduce_coop_wide<S, BLOCK, WT>;
+    else return k_reduce_coop<S, BLOCK>;
 }
 
-template <int S, int WT>
+template <int S, int BLOCK, int WT>
 hipError_t reduce_persistent(const RArgs &a, const Table &t, int64_t cap, hipStream_t s,
                              bool &launched) {
-    constexpr auto coop = coop_reduce_kernel<S, WT>();
-    int64_t resident = resident_groups<coop>(R_BLOCK);
+    constexpr auto coop = coop_reduce_kernel<S, BLOCK, WT>();
+    int64_t resident = resident_groups<coop>(BLOCK);
     if (cap > 0 && cap < resident) resident = cap;
     launched = false;
     if (resident < t.big_max_count) return hipSuccess;
@@ -1694,19 +1695,19 @@ hipError_t reduce_persistent(const RArgs &a, const Table &t, int64_t cap, hipStr
     c.n_small = t.n_small;
     c.tiles = t.d_big;
     c.n_tiles = t.n_big;
-    const int64_t small_groups = (t.n_small + R_BLOCK / 64 - 1) / (R_BLOCK / 64);
+    const int64_t small_groups = (t.n_small + BLOCK / 64 - 1) / (BLOCK / 64);
     const int64_t groups = t.n_big > small_groups ? t.n_big : small_groups;
     launched = true;
-    return launch_persistent(coop, groups < resident ? groups : resident, R_BLOCK, c, s);
+    return launch_persistent(coop, groups < resident ? groups : resident, BLOCK, c, s);
 }
 
-template <int S>
+template <int S, int BLOCK>
 hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free, hipStream_t s,
                        int64_t cap) {
-    const dim3 block(R_BLOCK);
+    const dim3 block(BLOCK);
     if (!requantize) {
         a.list = nullptr;
-        hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
+        hipLaunchKernelGGL((k_reduce<S, BLOCK, R_SUM>), dim3(static_cast<unsigned>(t.n_tiles)),
                            block, 0, s, a);
         return hipGetLastError();
     }
@@ -1725,26 +1726,26 @@ hipError_t reduce_geom(RArgs a, const Table &t, bool requantize, bool wait_free,
             RArgs c = a;
             c.tiles = t.d_rest;
             c.n_tiles = t.n_rest;
-            hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_rest)), block, 0, s, c);
+            hipLaunchKernelGGL((k_reduce<S, BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_rest)), block, 0, s, c);
         }
         return hipGetLastError();
     }
     if (!wait_free) {
         bool launched = false;
         hipError_t e;
-        if (S == R_SLOTS_WIDE && a.W == 8) e = reduce_persistent<S, 8>(a, t, cap, s, launched);
-        else if (S == R_SLOTS_WIDE && a.W == 16) e = reduce_persistent<S, 16>(a, t, cap, s, launched);
-        else e = reduce_persistent<S, 0>(a, t, cap, s, launched);
+        if (S == R_SLOTS_WIDE && a.W == 8) e = reduce_persistent<S, BLOCK, 8>(a, t, cap, s, launched);
+        else if (S == R_SLOTS_WIDE && a.W == 16) e = reduce_persistent<S, BLOCK, 16>(a, t, cap, s, launched);
+        else e = reduce_persistent<S, BLOCK, 0>(a, t, cap, s, launched);
         if (launched || e != hipSuccess) return e;
     }
     if (t.n_multi > 0) {
         RArgs p = a;
         p.list = t.d_multi;
-        hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_PASS1>), dim3(static_cast<unsigned>(t.n_multi)),
+        hipLaunchKernelGGL((k_reduce<S, BLOCK, R_PASS1>), dim3(static_cast<unsigned>(t.n_multi)),
                            block, 0, s, p);
     }
     a.list = nullptr;
-    hipLaunchKernelGGL((k_reduce<S, R_BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
+    hipLaunchKernelGGL((k_reduce<S, BLOCK, R_FUSED>), dim3(static_cast<unsigned>(t.n_tiles)),
                        block, 0, s, a);
     return hipGetLastError();
 }
@@ -1767,16 +1768,20 @@ int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t) {
     return mul ? quantize_resident_typed<__half, true>(t) : quantize_resident_typed<__half, false>(t);
 }
 
+template <int BLOCK>
+int64_t wide_resident() {
+    int64_t r = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, BLOCK, 0>()>(BLOCK);
+    const int64_t r8 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, BLOCK, 8>()>(BLOCK);
+    const int64_t r16 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, BLOCK, 16>()>(BLOCK);
+    if (r8 < r) r = r8;
+    if (r16 < r) r = r16;
+    return r;
+}
+
 int64_t reduce_resident(const Table &t) {
-    if (t.slots == R_SLOTS_WIDE) {
-        int64_t r = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 0>()>(R_BLOCK);
-        const int64_t r8 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 8>()>(R_BLOCK);
-        const int64_t r16 = resident_groups<coop_reduce_kernel<R_SLOTS_WIDE, 16>()>(R_BLOCK);
-        if (r8 < r) r = r8;
-        if (r16 < r) r = r16;
-        return r;
-    }
-    return resident_groups<coop_reduce_kernel<R_SLOTS_NARROW>()>(R_BLOCK);
+    if (t.block == R_BLOCK_CHUNK) return wide_resident<R_BLOCK_CHUNK>();
+    if (t.slots == R_SLOTS_WIDE) return wide_resident<R_BLOCK>();
+    return resident_groups<coop_reduce_kernel<R_SLOTS_NARROW, R_BLOCK>()>(R_BLOCK);
 }
 
 int64_t device_cus() { return device_info().cus; }
@@ -1798,7 +1803,8 @@ bool reduce_waits(const Table &t, int64_t cap) {
 hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool wait_free,
                          hipStream_t s, int64_t cap) {
     if (!table_ready(t, 1)) return hipErrorInvalidValue;
-    if (t.block != R_BLOCK || (t.slots != R_SLOTS_NARROW && t.slots != R_SLOTS_WIDE))
+    const bool chunk = t.block == R_BLOCK_CHUNK && t.slots == R_SLOTS_WIDE;
+    if (!chunk && (t.block != R_BLOCK || (t.slots != R_SLOTS_NARROW && t.slots != R_SLOTS_WIDE)))
         return hipErrorInvalidValue;
     RArgs a = a0;
     a.tiles = t.d_tiles;
@@ -1808,9 +1814,10 @@ hipError_t launch_reduce(const RArgs &a0, const Table &t, bool requantize, bool 
     a.res = t.d_res;
     a.cnt = t.d_cnt;
     a.ctl = t.d_ctl;
+    if (chunk) return reduce_geom<R_SLOTS_WIDE, R_BLOCK_CHUNK>(a, t, requantize, wait_free, s, cap);
     if (t.slots == R_SLOTS_WIDE)
-        return reduce_geom<R_SLOTS_WIDE>(a, t, requantize, wait_free, s, cap);
-    return reduce_geom<R_SLOTS_NARROW>(a, t, requantize, wait_free, s, cap);
+        return reduce_geom<R_SLOTS_WIDE, R_BLOCK>(a, t, requantize, wait_free, s, cap);
+    return reduce_geom<R_SLOTS_NARROW, R_BLOCK>(a, t, requantize, wait_free, s, cap);
 }
 
 }  // namespace gq

@@ -457,6 +457,51 @@ def test_narrow_reduce_tiles(gq, oracle, W):
     assert gq.gq_units_reduce_tile(step.units) == 8192
 
 
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("W", [3, 16])
+def test_chunk_wide_reduce_tiles(gq, oracle, kind, W):
+    """A table of units of about one 128 KiB fp32 chunk (16385 to 32768
+    elements) takes chunk-wide reduce tiles of 32768 elements on 1024-thread
+    work groups, each such unit one tile; units of exactly one, two and
+    three such tiles (the last two exchange their max), one element more
+    and less, units at the wide-tile limit, and small units sit among them,
+    at offsets off the 16-byte slots."""
+    rng = np.random.default_rng(91 + 2 * W + kind)
+    lens = [int(v) for v in rng.integers(16385, 32769, 60)]
+    for m in (1, 2, 3):
+        lens += [32768 * m - 1, 32768 * m, 32768 * m + 1]
+    lens += [1, 7, 2048, 2049, 4096, 16383, 16384, 16385]
+    rng.shuffle(lens)
+    lens = [3] + lens
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(W)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    step = _run_and_compare(gq, oracle, xs, kind, off, in_mul, "chunk_wide_k%d_W%d" % (kind, W))
+    assert gq.gq_units_reduce_tile(step.units) == 32768
+    assert gq.gq_units_launch_plan(step.units, kind, in_mul)["r_form"] == gq.GQ_FORM_PERSISTENT
+
+
+def test_chunk_wide_unit_larger_than_resident_groups(gq, oracle):
+    """A chunk-wide reduce table with one unit of one chunk-wide tile more
+    than the device keeps resident work groups: the reduce takes the
+    two-launch form on 1024-thread work groups."""
+    rng = np.random.default_rng(97)
+    probe = gq.gq_units_create(np.array([0, 32768, 65536, 98304], dtype=np.int64))
+    assert gq.gq_units_reduce_tile(probe) == 32768
+    G = gq.gq_units_launch_plan(probe, gq.GQ_F32, 1.0)["r_groups"]
+    say("resident chunk-wide reduce groups", G)
+    assert G >= 256
+    lens = [32768] * (G + 8) + [(G + 1) * 32768, 5000, 7]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    units = gq.gq_units_create(off)
+    assert gq.gq_units_reduce_tile(units) == 32768
+    assert gq.gq_units_launch_plan(units, gq.GQ_F32, 1.0)["r_form"] == gq.GQ_FORM_TWO_PASS
+    xs = [_grad(rng, n, F32) for _ in range(2)]
+    _run_and_compare(gq, oracle, xs, F32, off, 1.0, "chunk_wide_two_pass", modes=("fused",))
+
+
 def test_fp16_sixty_four_ranks(gq, oracle):
     """The largest rank count with loss-scaled fp16 inputs."""
     rng = np.random.default_rng(61)
@@ -483,8 +528,8 @@ def _random_table(rng, n_target):
 def test_random_tables_sweep(gq, oracle):
     """Seeded random unit tables, rank counts and element types through the
     fused step (the benchmark's launch shape, with the sum kept): every case
-    bit-exact, and every pairing of quantize schedule and reduce tile width
-    reached."""
+    bit-exact, and every pairing of quantize schedule and narrow or wide
+    reduce tiles reached."""
     rng = np.random.default_rng(2024)
     seen = set()
     for c in range(120):
@@ -507,7 +552,10 @@ def test_random_tables_sweep(gq, oracle):
             want = dict(want, q=[q[s0:] for q in want["q"]], r=want["r"][s0:],
                         q_out=want["q_out"][s0:])
         compare_step(got, want, W, check_r=True, label="sweep%d" % c)
-    assert len(seen) == 4, seen
+    # every quantize schedule with each of the narrow and wide reduce
+    # tiles (chunk-wide tiles, when a table takes them, come on top)
+    assert {(sc, rt) for sc in (gq.GQ_SCHED_LAYER, gq.GQ_SCHED_CHUNK)
+            for rt in (8192, 16384)} <= seen, seen
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])

@@ -92,7 +92,9 @@ def test_workload_every_element_large(gq, oracle, cfg):
         say("  rank", r, "generated and uploaded")
     step = GpuStep(gq, off, w.W, kind, w.n)
     assert gq.gq_units_schedule(step.units, kind) == gq.GQ_SCHED_CHUNK
-    assert gq.gq_units_reduce_tile(step.units) == 16384
+    # 128 KiB fp32 chunks fill one chunk-wide reduce tile; 64 Ki-element
+    # fp16 chunks span four wide ones
+    assert gq.gq_units_reduce_tile(step.units) == (32768 if kind == F32 else 16384)
     plan = gq.gq_units_launch_plan(step.units, kind, w.in_mul)
     assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_PERSISTENT, plan
     step.quantize(dx, w.in_mul)
