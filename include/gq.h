@@ -164,8 +164,10 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 
 /*
  * gq_units_reduce_tile -- elements per work-group tile of a table's reduce:
+ * 32768 (chunk-wide tiles, when most elements sit in units of 16385 to
+ * 32768 elements, e.g. 128 KiB fp32 chunks: each such unit one tile),
  * 16384 (wide tiles, when most elements sit in units wider than 8192
- * elements: per-layer and per-chunk scales) or 8192 (narrow tiles, for
+ * elements: per-layer scales, fp16 chunks) or 8192 (narrow tiles, for
  * tables of short units).  Chosen when the table is created; results do
  * not depend on it.  elems: host pointer receiving the number.
  */
