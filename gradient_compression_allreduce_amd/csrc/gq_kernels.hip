@@ -261,7 +261,8 @@ __device__ __forceinline__ uint32_t launch_tag(const uint32_t *ctl) {
 }
 
 // Thread 0: take the next ticket (every work group takes tickets until one
-// is past the end; the last work group to leave clears the counter).  Where
+// is past the end, or none where its first ticket is static and the grid has
+// a work group per tile; the last work group to leave clears the counter).  Where
 // each work group's first ticket is its own index (no atomic at the start:
 // the reduce and the layer quantize, whose start then costs no contended
 // round trip), the counter hands out tickets from base = G on.  The chunk
@@ -631,7 +632,9 @@ void k_quantize_layer(const QArgs a) {
         else
             quantize_parked_mode<TIn, S, BLOCK, MUL, CM_ZERO>(park, tp, a.in_mul, qp, a.q[wp]);
     };
-    bool tickets_left = true;
+    // with a grid of at least one work group per tile, the static first
+    // tickets cover every tile: no dynamic ticket (and no round trip for it)
+    bool tickets_left = static_cast<int64_t>(gridDim.x) < total;
     {
         const int64_t tk = blockIdx.x;
         if (tk < total) {
@@ -1123,7 +1126,9 @@ void k_reduce_coop(const RArgs a) {
             arr_c = unit_publish(a.pub, a.cnt + tc.slot, static_cast<int32_t>(tk), mc, tag);
     }
     while (tk < total) {
-        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl, gridDim.x);
+        if (threadIdx.x == 0)  // (no dynamic ticket if the static ones cover every tile)
+            s_val[1] = static_cast<int64_t>(gridDim.x) < total ? take_ticket(a.ctl, gridDim.x)
+                                                               : static_cast<uint32_t>(total);
         __syncthreads();
         const int64_t tn = s_val[1];
         const bool more = tn < total;
@@ -1226,7 +1231,9 @@ void k_reduce_coop_wide(const RArgs a) {
         put(acc);
     }
     while (tk < total) {
-        if (threadIdx.x == 0) s_val[1] = take_ticket(a.ctl, gridDim.x);
+        if (threadIdx.x == 0)  // (no dynamic ticket if the static ones cover every tile)
+            s_val[1] = static_cast<int64_t>(gridDim.x) < total ? take_ticket(a.ctl, gridDim.x)
+                                                               : static_cast<uint32_t>(total);
         __syncthreads();
         const int64_t tn = s_val[1];
         const bool more = tn < total;

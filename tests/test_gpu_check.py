@@ -179,6 +179,30 @@ def test_error_report_random_units(gq, oracle):
     assert _same_f64(got, again)
 
 
+def test_error_report_chunk_wide_units(gq, oracle):
+    """The report on a table of 128 KiB fp32 chunks, which takes chunk-wide
+    reduce tiles of 32768 elements (one work group of the report per tile,
+    so each group strides over four times its lanes): units of one, two and
+    three such tiles and one element more and less, off the 16-byte slots."""
+    rng = np.random.default_rng(312)
+    lens = [int(v) for v in rng.integers(16385, 32769, 24)]
+    for m in (1, 2, 3):
+        lens += [32768 * m - 1, 32768 * m, 32768 * m + 1]
+    rng.shuffle(lens)
+    lens = [5] + lens
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    W = 3
+    xs = _grads(rng, n, W, F32)
+    res = oracle.allreduce_step(xs, F32, off)
+    ref = oracle.sum_f32(xs, F32)
+    units = gq.gq_units_create(off)
+    assert gq.gq_units_reduce_tile(units) == 32768
+    got = _report_on_gpu(gq, units, res["q_out"], res["scale_out"], ref)
+    want = oracle.error_report(res["q_out"], res["scale_out"], ref, off)
+    compare_report(got, want, res["q_out"], res["scale_out"], ref, off, "chunk_wide")
+
+
 def test_error_report_edge_units(gq, oracle):
     """All-zero units, zero codes against a nonzero reference, identical and
     negated vectors (cos exactly 1 and -1), a NaN and an inf reference, and
