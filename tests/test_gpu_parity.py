@@ -586,7 +586,8 @@ def test_tiny_unit_packs(gq, oracle, kind, W):
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
-@pytest.mark.parametrize("W,wide", [(1, False), (3, False), (16, False), (64, False), (5, True)])
+@pytest.mark.parametrize("W,wide", [(1, False), (3, False), (16, False), (64, False), (5, True),
+                                    (5, "chunk")])
 def test_short_unit_tables(gq, oracle, kind, W, wide):
     """Tables of many short tensors (every unit fits one tile, units of one
     wave's share hold most elements) take the wait-free short-unit form in
@@ -596,11 +597,16 @@ def test_short_unit_tables(gq, oracle, kind, W, wide):
     unit.  Units of 1 .. 4096 elements at every offset, some spanning one
     slot more than 64 * 16, some of exactly eight pieces, some all zero;
     with `wide`, also units of 9 .. 16 pieces (one wide reduce tile each)
-    and units above 64 * 17 quantize slots."""
+    and units above 64 * 17 quantize slots; with `wide` = "chunk", units of
+    17 .. 32 pieces instead (one chunk-wide reduce tile each)."""
     rng = np.random.default_rng(600 + W + 10 * kind)
     lens = list(rng.integers(1, 2049 if wide else 4097, 900))
     lens += [4096, 4095, 4097, 8000, 8176, 2049, 1, 2] * 3
-    if wide:
+    if wide == "chunk":
+        # most elements of the units above 2048 in units of 16385 .. 32752
+        # (at most 2048 slots at any offset): chunk-wide reduce tiles
+        lens += [16385, 20000, 32752, 24000, 30000, 28000] * 2
+    elif wide:
         # most elements of the units above 2048 in units above 8192: wide
         # reduce tiles, whose small units are those of at most 128 slots
         lens += [8193, 12000, 16000, 9000, 15000, 8192, 8191] * 2
@@ -615,4 +621,6 @@ def test_short_unit_tables(gq, oracle, kind, W, wide):
     in_mul = 2.0 ** -16 if kind == F16 else 1.0
     plan = gq.gq_units_launch_plan(units, kind, in_mul)
     assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_SHORT_UNITS, plan
+    if wide == "chunk":
+        assert gq.gq_units_reduce_tile(units) == 32768
     _run_and_compare(gq, oracle, xs, kind, off, in_mul, "short_units_W%d_k%d" % (W, kind))
