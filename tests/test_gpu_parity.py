@@ -458,7 +458,7 @@ def test_narrow_reduce_tiles(gq, oracle, W):
 
 
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
-@pytest.mark.parametrize("W", [3, 8, 16])
+@pytest.mark.parametrize("W", [3, 8, 16, 64])
 def test_chunk_wide_reduce_tiles(gq, oracle, kind, W):
     """A table of units of about one 128 KiB fp32 chunk (16385 to 32768
     elements) takes chunk-wide reduce tiles of 32768 elements on 1024-thread
