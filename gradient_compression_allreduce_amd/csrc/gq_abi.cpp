@@ -410,6 +410,16 @@ gq_status gq_units_create(const int64_t *h_off, int64_t n_units, gq_units **out)
             t.sched = (mostly_small || 2 * in_chunk >= in_big) ? gq::SCHED_CHUNK : gq::SCHED_LAYER;
             t.block = t.sched == gq::SCHED_CHUNK ? gq::Q_BLOCK_CHUNK : gq::Q_BLOCK_LAYER;
             t.slots = t.sched == gq::SCHED_CHUNK ? gq::Q_SLOTS_CHUNK : gq::Q_SLOTS_LAYER;
+            if (t.sched == gq::SCHED_CHUNK) {
+                // 8-row chunk tiles where that adds no tile to any unit
+                const int64_t short_cap =
+                    static_cast<int64_t>(gq::Q_BLOCK_CHUNK) * gq::Q_SLOTS_CHUNK_SHORT;
+                bool same = true;
+                for (int64_t u = 0; u < n_units && same; ++u)
+                    if (span(u) > small_cap)
+                        same = (span(u) + short_cap - 1) / short_cap == (span(u) + cap - 1) / cap;
+                if (same) t.slots = gq::Q_SLOTS_CHUNK_SHORT;
+            }
         }
         std::vector<gq::Tile> tiles;
         std::vector<int32_t> multi, unit_first;

@@ -37,12 +37,18 @@ enum TableId { TAB_Q32 = 0, TAB_Q16 = 1, TAB_R = 2, TAB_COUNT = 3 };
 //  SCHED_CHUNK  units of about one tile (per-chunk scales, small tensors):
 //               1024-thread tiles of 144 KiB, which hold a whole chunk of
 //               the chunk plan for every tensor of 1 MiB or more (those
-//               chunks are below 128 KiB * 9/8); the next tile's loads are
-//               in flight while the current tile's codes are written.
+//               chunks are below 128 KiB * 9/8), or of 128 KiB where that
+//               adds no tile to any unit; the next tile's loads are in
+//               flight while the current tile's codes are written.
 enum Sched { SCHED_LAYER = 0, SCHED_CHUNK = 1 };
 
 constexpr int Q_SLOTS_LAYER = 8;     // 8 x 16 bytes per thread
 constexpr int Q_SLOTS_CHUNK = 9;     // 9 x 16 bytes per thread
+// Chunk tiles of 8 rows (128 KiB) where no unit needs more tiles of that
+// size than of 9 rows, e.g. tables of whole 128 KiB fp32 chunks, whose
+// ninth row would stay empty in every tile: the same tiles, one row of
+// loads and checks fewer per lane.
+constexpr int Q_SLOTS_CHUNK_SHORT = 8;
 constexpr int Q_BLOCK_LAYER = 512;   // fp32: 16384 elements per tile (64 KiB)
 constexpr int Q_BLOCK_CHUNK = 1024;  // fp32: 36864 elements per tile (144 KiB)
 constexpr int R_BLOCK = 512;

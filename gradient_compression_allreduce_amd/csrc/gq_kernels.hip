@@ -1560,21 +1560,18 @@ hipError_t launch_persistent(K kernel, int64_t groups, int block, const A &args,
     return hipGetLastError();
 }
 
-template <int BLOCK>
-constexpr int q_slots() { return BLOCK == Q_BLOCK_CHUNK ? Q_SLOTS_CHUNK : Q_SLOTS_LAYER; }
-
-template <typename TIn, int BLOCK, bool MUL>
+template <typename TIn, int BLOCK, int S, bool MUL>
 constexpr auto coop_quantize_kernel() {
-    if constexpr (BLOCK == Q_BLOCK_CHUNK) return k_quantize_chunk<TIn, q_slots<BLOCK>(), BLOCK, MUL>;
-    else return k_quantize_layer<TIn, q_slots<BLOCK>(), BLOCK, MUL>;
+    if constexpr (BLOCK == Q_BLOCK_CHUNK) return k_quantize_chunk<TIn, S, BLOCK, MUL>;
+    else return k_quantize_layer<TIn, S, BLOCK, MUL>;
 }
 
-template <typename TIn, int BLOCK, bool MUL>
+template <typename TIn, int BLOCK, int S, bool MUL>
 hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s, int64_t cap) {
     const dim3 block(BLOCK);
     const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
     if (a.amax != nullptr) {
-        hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<TIn, S, BLOCK, MUL, Q_GIVEN>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (short_table(t)) {
@@ -1594,12 +1591,12 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s, int64_t 
             QArgs c = a;
             c.tiles = t.d_rest;
             c.n_tiles = t.n_rest;
-            hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_FUSED>),
+            hipLaunchKernelGGL((k_quantize<TIn, S, BLOCK, MUL, Q_FUSED>),
                                dim3(static_cast<unsigned>(t.n_rest), static_cast<unsigned>(a.W)), block, 0, s, c);
         }
         return hipGetLastError();
     }
-    constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, MUL>();
+    constexpr auto coop = coop_quantize_kernel<TIn, BLOCK, S, MUL>();
     int64_t resident = resident_groups<coop>(BLOCK);
     if (cap > 0 && cap < resident) resident = cap;
     if (resident >= t.big_max_count) {
@@ -1617,9 +1614,9 @@ hipError_t quantize_geom(const QArgs &a, const Table &t, hipStream_t s, int64_t 
     // a unit with more tiles than resident work groups: two launches
     QArgs p = a;
     p.list = t.d_multi;
-    hipLaunchKernelGGL((k_tile_absmax<TIn, q_slots<BLOCK>(), BLOCK>),
+    hipLaunchKernelGGL((k_tile_absmax<TIn, S, BLOCK>),
                        dim3(static_cast<unsigned>(t.n_multi), static_cast<unsigned>(a.W)), block, 0, s, p);
-    hipLaunchKernelGGL((k_quantize<TIn, q_slots<BLOCK>(), BLOCK, MUL, Q_FUSED>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_quantize<TIn, S, BLOCK, MUL, Q_FUSED>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -1635,22 +1632,30 @@ hipError_t quantize_typed(const QArgs &a0, const Table &t, hipStream_t s, int64_
     a.n_multi_units = t.n_multi_units;
     a.small = t.d_small;
     a.n_small = t.n_small;
-    if (t.block == Q_BLOCK_CHUNK) return quantize_geom<TIn, Q_BLOCK_CHUNK, MUL>(a, t, s, cap);
-    return quantize_geom<TIn, Q_BLOCK_LAYER, MUL>(a, t, s, cap);
+    if (t.block == Q_BLOCK_CHUNK && t.slots == Q_SLOTS_CHUNK_SHORT)
+        return quantize_geom<TIn, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK_SHORT, MUL>(a, t, s, cap);
+    if (t.block == Q_BLOCK_CHUNK) return quantize_geom<TIn, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK, MUL>(a, t, s, cap);
+    return quantize_geom<TIn, Q_BLOCK_LAYER, Q_SLOTS_LAYER, MUL>(a, t, s, cap);
 }
 
-template <typename TIn, int BLOCK>
+template <typename TIn, int BLOCK, int S>
 void absmax_geom(const QArgs &a, const Table &t, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(t.n_tiles), static_cast<unsigned>(a.W));
-    hipLaunchKernelGGL((k_tile_absmax<TIn, q_slots<BLOCK>(), BLOCK>), grid, dim3(BLOCK), 0, s, a);
+    hipLaunchKernelGGL((k_tile_absmax<TIn, S, BLOCK>), grid, dim3(BLOCK), 0, s, a);
 }
 
 }  // namespace
 
 // ---- launchers ----------------------------------------------------------------------------
 
+// The quantize table geometries the launchers are built for.
+static bool quantize_geometry(const Table &t) {
+    if (t.block == Q_BLOCK_LAYER) return t.slots == Q_SLOTS_LAYER;
+    return t.block == Q_BLOCK_CHUNK && (t.slots == Q_SLOTS_CHUNK || t.slots == Q_SLOTS_CHUNK_SHORT);
+}
+
 hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream_t s) {
-    if (!table_ready(t, a0.n_units)) return hipErrorInvalidValue;
+    if (!table_ready(t, a0.n_units) || !quantize_geometry(t)) return hipErrorInvalidValue;
     QArgs a = a0;
     a.list = nullptr;
     a.partial = t.d_partial;
@@ -1660,13 +1665,16 @@ hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream
     const int64_t total = static_cast<int64_t>(a.W) * a.n_units;
     const unsigned nb = static_cast<unsigned>((total + 255) / 256);
     const bool chunk = t.block == Q_BLOCK_CHUNK;
+    const bool rows8 = chunk && t.slots == Q_SLOTS_CHUNK_SHORT;
     if (dt == GQ_F32) {
-        if (chunk) absmax_geom<float, Q_BLOCK_CHUNK>(a, t, s);
-        else absmax_geom<float, Q_BLOCK_LAYER>(a, t, s);
+        if (rows8) absmax_geom<float, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK_SHORT>(a, t, s);
+        else if (chunk) absmax_geom<float, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK>(a, t, s);
+        else absmax_geom<float, Q_BLOCK_LAYER, Q_SLOTS_LAYER>(a, t, s);
         hipLaunchKernelGGL(k_absmax_finalize<float>, dim3(nb), dim3(256), 0, s, a, mul);
     } else {
-        if (chunk) absmax_geom<__half, Q_BLOCK_CHUNK>(a, t, s);
-        else absmax_geom<__half, Q_BLOCK_LAYER>(a, t, s);
+        if (rows8) absmax_geom<__half, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK_SHORT>(a, t, s);
+        else if (chunk) absmax_geom<__half, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK>(a, t, s);
+        else absmax_geom<__half, Q_BLOCK_LAYER, Q_SLOTS_LAYER>(a, t, s);
         hipLaunchKernelGGL(k_absmax_finalize<__half>, dim3(nb), dim3(256), 0, s, a, mul);
     }
     return hipGetLastError();
@@ -1674,7 +1682,7 @@ hipError_t launch_absmax(const QArgs &a0, gq_dtype dt, const Table &t, hipStream
 
 hipError_t launch_quantize(const QArgs &a, gq_dtype dt, const Table &t, hipStream_t s,
                            int64_t cap) {
-    if (!table_ready(t, a.n_units)) return hipErrorInvalidValue;
+    if (!table_ready(t, a.n_units) || !quantize_geometry(t)) return hipErrorInvalidValue;
     const bool mul = a.in_mul != 1.0f;
     if (dt == GQ_F32)
         return mul ? quantize_typed<float, true>(a, t, s, cap)
@@ -1764,9 +1772,14 @@ hipError_t launch_copy_word(const uint32_t *src, uint32_t *dst, hipStream_t s) {
 
 template <typename TIn, bool MUL>
 int64_t quantize_resident_typed(const Table &t) {
+    if (t.block == Q_BLOCK_CHUNK && t.slots == Q_SLOTS_CHUNK_SHORT)
+        return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK_SHORT, MUL>()>(
+            Q_BLOCK_CHUNK);
     if (t.block == Q_BLOCK_CHUNK)
-        return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_CHUNK, MUL>()>(Q_BLOCK_CHUNK);
-    return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_LAYER, MUL>()>(Q_BLOCK_LAYER);
+        return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_CHUNK, Q_SLOTS_CHUNK, MUL>()>(
+            Q_BLOCK_CHUNK);
+    return resident_groups<coop_quantize_kernel<TIn, Q_BLOCK_LAYER, Q_SLOTS_LAYER, MUL>()>(
+        Q_BLOCK_LAYER);
 }
 
 int64_t quantize_resident(gq_dtype dt, bool mul, const Table &t) {

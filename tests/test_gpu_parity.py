@@ -502,6 +502,34 @@ def test_chunk_wide_unit_larger_than_resident_groups(gq, oracle):
     _run_and_compare(gq, oracle, xs, F32, off, 1.0, "chunk_wide_two_pass", modes=("fused",))
 
 
+@pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("W", [3, 16])
+def test_chunk_tiles_of_eight_rows(gq, oracle, kind, W):
+    """Per-chunk units of whole 128 KiB chunks (tensors of whole chunks on
+    16-byte boundaries), where every chunk fills 8 rows of a chunk tile:
+    the table takes 8-row chunk tiles (no unit needs more tiles of 8 rows
+    than of 9), with small tensors and a unit of two tiles among them."""
+    rng = np.random.default_rng(71 + 2 * W + kind)
+    esz = 4 if kind == F32 else 2
+    chunk = (128 * 1024) // esz
+    sizes = [chunk * 8, 40, chunk * 3, chunk, 1000, chunk * 5, 7]
+    parts = [np.zeros(1, np.int64)]
+    base = 0
+    for sz in sizes:
+        parts.append(gq.gq_plan_chunks(sz, esz)[1:] + base)
+        base += sz
+    off = np.concatenate(parts)
+    assert np.all(np.diff(off)[np.diff(off) > 64 * 16 * 16 // esz] == chunk)
+    # one unit of two tiles in either geometry, at an offset off the slots
+    off = np.concatenate([off, [off[-1] + 2 * chunk - 16]])
+    n = int(off[-1])
+    xs = [_grad(rng, n, kind) for _ in range(W)]
+    in_mul = 2.0 ** -16 if kind == F16 else 1.0
+    units = gq.gq_units_create(off)
+    assert gq.gq_units_schedule(units, kind) == gq.GQ_SCHED_CHUNK
+    _run_and_compare(gq, oracle, xs, kind, off, in_mul, "rows8_k%d_W%d" % (kind, W))
+
+
 def test_fp16_sixty_four_ranks(gq, oracle):
     """The largest rank count with loss-scaled fp16 inputs."""
     rng = np.random.default_rng(61)
