@@ -531,6 +531,16 @@ gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched) {
     return ok();
 }
 
+gq_status gq_units_quantize_tile(const gq_units *u, gq_dtype dt, int64_t *elems) {
+    const char *op = "gq_units_quantize_tile";
+    if (!u) return fail(GQ_ERR_INVALID, op, "unit table is NULL");
+    if (!elems) return fail(GQ_ERR_INVALID, op, "elems is NULL");
+    if (dt != GQ_F32 && dt != GQ_F16) return fail(GQ_ERR_INVALID, op, "unknown dtype %d", (int)dt);
+    const gq::Table &t = u->tab[q_table(dt)];
+    *elems = static_cast<int64_t>(t.block) * t.slots * gq::kSlotElems[q_table(dt)];
+    return ok();
+}
+
 gq_status gq_units_reduce_tile(const gq_units *u, int64_t *elems) {
     const char *op = "gq_units_reduce_tile";
     if (!u) return fail(GQ_ERR_INVALID, op, "unit table is NULL");

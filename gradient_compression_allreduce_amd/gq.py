@@ -29,7 +29,7 @@ GQ_NOALLOC_MAX_MAXIMA = 1 << 20
 CHUNK_BYTES, ALIGN_BYTES = 131072, 64
 
 EXPORTS = ("gq_last_error", "gq_version", "gq_plan_chunks", "gq_units_create",
-           "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_reduce_tile", "gq_units_faults",
+           "gq_units_destroy", "gq_units_info", "gq_units_schedule", "gq_units_quantize_tile", "gq_units_reduce_tile", "gq_units_faults",
            "gq_units_faults_async", "gq_units_launch_plan", "gq_units_clear_faults", "gq_units_force_timeout",
            "gq_absmax", "gq_quantize", "gq_quantize_noalloc",
            "gq_reduce_dequant", "gq_requantize", "gq_reduce_requantize",
@@ -68,6 +68,8 @@ def _load():
     L.gq_units_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.gq_units_schedule.restype = st
     L.gq_units_schedule.argtypes = [vp, i32, ctypes.POINTER(i32)]
+    L.gq_units_quantize_tile.restype = st
+    L.gq_units_quantize_tile.argtypes = [vp, i32, ctypes.POINTER(i64)]
     L.gq_units_reduce_tile.restype = st
     L.gq_units_reduce_tile.argtypes = [vp, ctypes.POINTER(i64)]
     L.gq_units_faults.restype = st
@@ -361,9 +363,17 @@ def gq_units_schedule(units, dtype_code=GQ_F32):
     return v.value
 
 
+def gq_units_quantize_tile(units, dtype_code=GQ_F32):
+    """Elements of the given type per work-group tile of the table's fused
+    quantize, chosen when the table was created."""
+    v = ctypes.c_int64(0)
+    _check(lib.gq_units_quantize_tile(units.handle, dtype_code, ctypes.byref(v)))
+    return v.value
+
+
 def gq_units_reduce_tile(units):
-    """Elements per work-group tile of the table's reduce (8192 or 16384),
-    chosen when the table was created."""
+    """Elements per work-group tile of the table's reduce (8192, 16384 or
+    32768), chosen when the table was created."""
     v = ctypes.c_int64(0)
     _check(lib.gq_units_reduce_tile(units.handle, ctypes.byref(v)))
     return v.value

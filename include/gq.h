@@ -163,6 +163,16 @@ gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
 gq_status gq_units_schedule(const gq_units *u, gq_dtype dt, int32_t *sched);
 
 /*
+ * gq_units_quantize_tile -- elements of type dt per work-group tile of a
+ * table's fused quantize: 64 KiB of input under GQ_SCHED_LAYER; under
+ * GQ_SCHED_CHUNK 144 KiB, or 128 KiB where no unit needs more tiles of that
+ * size (e.g. whole 128 KiB fp32 chunks: 32768 fp32 elements).  Chosen when
+ * the table is created; results do not depend on it.  elems: host pointer
+ * receiving the number.
+ */
+gq_status gq_units_quantize_tile(const gq_units *u, gq_dtype dt, int64_t *elems);
+
+/*
  * gq_units_reduce_tile -- elements per work-group tile of a table's reduce:
  * 32768 (chunk-wide tiles, when most elements sit in units of 16385 to
  * 32768 elements, e.g. 128 KiB fp32 chunks: each such unit one tile),

@@ -129,6 +129,7 @@ def test_argument_errors_before_any_device_call(gq):
     v32, v64 = ctypes.c_int32(0), ctypes.c_int64(0)
     assert L.gq_units_schedule(null, gq.GQ_F32, ctypes.byref(v32)) == gq.GQ_ERR_INVALID
     assert L.gq_units_reduce_tile(null, ctypes.byref(v64)) == gq.GQ_ERR_INVALID
+    assert L.gq_units_quantize_tile(null, gq.GQ_F32, ctypes.byref(v64)) == gq.GQ_ERR_INVALID
     assert "unit table" in gq.gq_last_error()
     assert L.gq_units_force_timeout(null) == gq.GQ_ERR_INVALID
     assert "unit table" in gq.gq_last_error()

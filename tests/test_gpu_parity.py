@@ -527,6 +527,7 @@ def test_chunk_tiles_of_eight_rows(gq, oracle, kind, W):
     in_mul = 2.0 ** -16 if kind == F16 else 1.0
     units = gq.gq_units_create(off)
     assert gq.gq_units_schedule(units, kind) == gq.GQ_SCHED_CHUNK
+    assert gq.gq_units_quantize_tile(units, kind) == 1024 * 8 * (16 // esz)
     _run_and_compare(gq, oracle, xs, kind, off, in_mul, "rows8_k%d_W%d" % (kind, W))
 
 

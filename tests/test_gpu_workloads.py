@@ -95,6 +95,9 @@ def test_workload_every_element_large(gq, oracle, cfg):
     # 128 KiB fp32 chunks fill one chunk-wide reduce tile; 64 Ki-element
     # fp16 chunks span four wide ones
     assert gq.gq_units_reduce_tile(step.units) == (32768 if kind == F32 else 16384)
+    # whole 128 KiB fp32 chunks fill 8 rows of a chunk quantize tile; the
+    # fp16 table's 65,664-element chunks need 9
+    assert gq.gq_units_quantize_tile(step.units, kind) == (32768 if kind == F32 else 73728)
     plan = gq.gq_units_launch_plan(step.units, kind, w.in_mul)
     assert plan["q_form"] == plan["r_form"] == gq.GQ_FORM_PERSISTENT, plan
     step.quantize(dx, w.in_mul)
