@@ -151,7 +151,8 @@ gq_status gq_units_info(const gq_units *u, int64_t *n, int64_t *n_units);
 /*
  * gq_units_schedule -- which schedule the fused quantize of a table uses for
  * elements of type dt.  GQ_SCHED_CHUNK (144 KiB tiles, which hold a 128 KiB
- * chunk of every tensor of 1 MiB or more) when most elements of the
+ * chunk of every tensor of 1 MiB or more; 128 KiB tiles where that adds no
+ * tile to any unit, see gq_units_quantize_tile) when most elements of the
  * non-small units sit in units that fit one such tile but not one 64 KiB
  * tile (per-chunk scales), or when small units (one wave's share) hold most
  * elements; GQ_SCHED_LAYER (64 KiB tiles) otherwise: per-tensor or
