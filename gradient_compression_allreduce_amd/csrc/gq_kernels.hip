@@ -479,6 +479,7 @@ void k_quantize_chunk(const QArgs a) {
     using Raw = typename In<TIn>::Raw;
     __shared__ uint32_t sh[BLOCK / 64];
     __shared__ uint32_t s_val[2];  // unit max, ticket
+    __shared__ uint32_t s_tk[2];   // early tickets, by iteration parity
     const int64_t total = static_cast<int64_t>(a.W) * a.n_tiles;
     const uint32_t tag = launch_tag(a.ctl);
     Raw cur[S], nxt[S];
@@ -530,6 +531,7 @@ void k_quantize_chunk(const QArgs a) {
             return t;
         };
         int64_t tn = ticket_after();
+        int par = 0;
         for (;;) {
             const bool more = tn < total;
             int wn = 0;
@@ -548,13 +550,19 @@ void k_quantize_chunk(const QArgs a) {
             if (threadIdx.x == 0 && tix == tc.first) a.scale[wc][tc.unit] = sc;
             quantize_tile<TIn, S, BLOCK, MUL>(cur, tc, a.in_mul, quant_params(sc, true), a.q[wc]);
             if (!more) break;
+            // an early ticket reaches the work group through LDS at the
+            // block-max barrier inside tile_max, with no barriers of its
+            // own; slots alternate by parity, since the next write to a slot
+            // follows another tile_max barrier, after every read of it
+            if (early && threadIdx.x == 0) s_tk[par] = pend;
             mc = tile_max(nxt, tnx, wn, tixn);
 #pragma unroll
             for (int s = 0; s < S; ++s) cur[s] = nxt[s];
             tc = tnx;
             wc = wn;
             tix = tixn;
-            tn = ticket_after();
+            tn = early ? static_cast<int64_t>(s_tk[par]) : next_ticket();
+            par ^= 1;
         }
     }
     small_phase<BLOCK>(static_cast<int64_t>(a.W) * a.n_small, [&](int64_t item) {
