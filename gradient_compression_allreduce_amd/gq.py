@@ -333,10 +333,11 @@ class Units:
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
-        if _finalizing():
-            return
+        # (at interpreter shutdown this module's globals may already be
+        # None; the exit hook has freed the handle by then)
         try:
-            self.close()
+            if not _finalizing():
+                self.close()
         except Exception:
             pass
 
@@ -570,10 +571,11 @@ class Pipe:
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
-        if _finalizing():
-            return
+        # (at interpreter shutdown this module's globals may already be
+        # None; the exit hook has freed the handle by then)
         try:
-            self.close()
+            if not _finalizing():
+                self.close()
         except Exception:
             pass
 
@@ -647,10 +649,11 @@ class Chunker:
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
-        if _finalizing():
-            return
+        # (at interpreter shutdown this module's globals may already be
+        # None; the exit hook has freed the handle by then)
         try:
-            self.close()
+            if not _finalizing():
+                self.close()
         except Exception:
             pass
 
