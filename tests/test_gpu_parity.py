@@ -587,6 +587,41 @@ def test_random_tables_sweep(gq, oracle):
             for rt in (8192, 16384)} <= seen, seen
 
 
+def test_random_chunk_plan_sweep(gq, oracle):
+    """Seeded per-chunk plans of random tensor lists (whole 128 KiB chunks,
+    or any length), rank counts and element types through the fused step:
+    every case bit-exact, and the 8-row chunk quantize tiles and the
+    chunk-wide reduce tiles both reached."""
+    rng = np.random.default_rng(3000)
+    seen = set()
+    for c in range(40):
+        kind = F32 if rng.random() < 0.6 else F16
+        W = int(rng.choice([1, 2, 3, 5, 8, 16]))
+        esz = 4 if kind == F32 else 2
+        chunk = (128 * 1024) // esz
+        sizes = [int(rng.integers(1, 4)) * chunk if rng.random() < 0.7
+                 else int(rng.integers(1, 2 * chunk)) for _ in range(int(rng.integers(1, 6)))]
+        parts, base = [np.zeros(1, np.int64)], 0
+        for sz in sizes:
+            parts.append(gq.gq_plan_chunks(sz, esz)[1:] + base)
+            base += sz
+        off = np.concatenate(parts)
+        n = int(off[-1])
+        xs = [_grad(rng, n, kind) for _ in range(W)]
+        in_mul = 2.0 ** -16 if kind == F16 else 1.0
+        step = GpuStep(gq, off, W, kind, n)
+        seen.add((gq.gq_units_quantize_tile(step.units, kind) * esz,
+                  gq.gq_units_reduce_tile(step.units)))
+        say("chunk plan case", c, "kind", kind, "W", W, "n", n, "units", off.size - 1)
+        want = oracle.allreduce_step(xs, kind, off, in_mul)
+        step.quantize([to_device(x) for x in xs], in_mul)
+        step.reduce(fused=True, with_r=True)
+        compare_step(step.host(), want, W, check_r=True, label="chunk_plan%d" % c)
+    # quantize tile bytes 128 KiB (8 rows) reached, and chunk-wide reduce tiles
+    assert any(qb == 128 * 1024 for qb, _ in seen), seen
+    assert any(rt == 32768 for _, rt in seen), seen
+
+
 @pytest.mark.parametrize("kind", [F32, F16], ids=["f32", "f16"])
 @pytest.mark.parametrize("W", [3, 8])
 def test_tiny_unit_packs(gq, oracle, kind, W):
